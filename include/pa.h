@@ -1,0 +1,189 @@
+/*
+ * pa.h - paged decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpa.so.  Two operations make up the hot path of PagedAttention:
+ *
+ *   pa_cache_write  stores each new token's key and value in the cache slot its
+ *                   slot id names.
+ *   pa_decode       single-query attention for every sequence of a batch, reading
+ *                   each sequence's keys and values through its block table.
+ *
+ * Pages cited (title, site):
+ *   [AB]  "什么是分页注意力（PagedAttention）？"                     aiboss88.com wiki
+ *   [CY]  "深入解析 PagedAttention：vLLM 显存优化的核心魔法"            cygnushan.xyz blog
+ *   [ASP] "PagedAttention"                                          awesome-system-papers
+ *   [RK]  "什么是 LLM 中的分页注意力(Paged Attention)?它是如何工作的?"  news.rkmt.cn
+ *
+ * ---- Storage (the pages fix no layout; this is the library's definition) ----
+ * The KV cache is a pool of N fixed-size physical blocks of block_size (bs) token
+ * slots each, for every KV head ([AB] 工作机制: the cache is cut into equal blocks
+ * that may sit anywhere; [ASP] 核心思想: e.g. 16 tokens a block).  Two device
+ * arrays, row-major, element type = the batch dtype:
+ *
+ *   k_cache [N][Hkv][bs][D]   one (block, KV head) tile holds bs key rows of D
+ *   v_cache [N][Hkv][D][bs]   one (block, KV head) tile holds D value columns
+ *
+ * so every (block, KV head) tile of either array is bs*D contiguous elements:
+ * inside a block, access stays contiguous ([ASP] 核心思想, the kernel rewrite).
+ * The value tile is stored dimension-major so the attention kernel's weighted
+ * sum over tokens reads whole 16-byte rows.
+ *
+ * Token t (0-based) of sequence s lives in physical block block_tables[s][t / bs]
+ * at in-block offset t % bs ([RK] 块表: logical blocks numbered 0, 1, 2 map to
+ * scattered physical blocks).  A slot id is phys * bs + offset.
+ *
+ * ---- Conventions -----------------------------------------------------------
+ * - Every pointer argument that names tensor data is a DEVICE pointer owned by
+ *   the caller; the library never allocates, frees or keeps memory, and keeps no
+ *   pointer after a call returns.  Tensor pointers must be 16-byte aligned.
+ * - Calls are asynchronous on the HIP stream given in the ext struct (NULL = the
+ *   null stream).  No call synchronises the host.
+ * - Every host-side argument is checked before anything is sent to the GPU; a
+ *   bad argument returns an error status and launches nothing.  pa_last_error()
+ *   then returns a readable reason.  No C++ exception crosses the ABI.
+ * - Supported: dtype f32, f16, bf16; head_dim 64 or 128; block_size 4, 8, 16 or
+ *   32; num_q_heads a multiple of num_kv_heads.  Anything else is
+ *   PA_ERR_UNSUPPORTED or PA_ERR_INVALID_ARG.
+ * - Calls are reentrant and thread-safe: no global mutable state beyond the
+ *   thread-local error text.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* a null pointer, a bad size, a misaligned pointer       */
+  PA_ERR_UNSUPPORTED = 2, /* valid but not built: dtype / head_dim / block_size ... */
+  PA_ERR_WORKSPACE = 3,   /* split-K workspace missing or smaller than required      */
+  PA_ERR_HIP = 4          /* the HIP runtime refused a launch; see pa_last_error()   */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Shapes and options of a pa_decode call that its positional arguments leave out. */
+typedef struct pa_decode_ext {
+  int32_t num_seqs;           /* S >= 0 (0: nothing to do) and <= 65535               */
+  int32_t num_q_heads;        /* Hq > 0, a multiple of num_kv_heads                    */
+  int32_t head_dim;           /* D: 64 or 128                                          */
+  int32_t max_blocks_per_seq; /* row stride of block_tables, >= 1                      */
+  int64_t num_blocks;         /* N, physical blocks in the pool, >= 1                  */
+  int32_t partition_size;     /* tokens per split-K partition: 0 = 512 (default),      */
+                              /* < 0 = never split, > 0 = that many (multiple of 32)  */
+  int32_t dtype;              /* pa_dtype of q, k_cache, v_cache and out               */
+  void* workspace;            /* device scratch for split-K partials (caller-owned)    */
+  size_t workspace_bytes;     /* its size; see pa_decode_workspace_bytes               */
+  void* stream;               /* hipStream_t                                           */
+} pa_decode_ext;
+
+/*
+ * pa_decode - single-query decode attention over the paged cache.
+ *
+ * For every sequence s and query head h (KV head g = h / (Hq / Hkv), consecutive
+ * grouping):
+ *     z_t = scale * <q[s][h], K_s[t]>,     t = 0 .. seq_lens[s] - 1
+ *     out[s][h] = sum_t exp(z_t - max z) V_s[t] / sum_t exp(z_t - max z)
+ * where K_s[t], V_s[t] are token t's key and value for KV head g, found through
+ * the block table.  Paging changes where K and V live, not this formula ([AB]
+ * 边界与常见误解, first point); the kernel takes the block table and gathers K and
+ * V block by block ([ASP] 实现要点, the custom kernel that accepts a block table).
+ * seq_lens[s] counts every token attended, including one just stored with
+ * pa_cache_write.  seq_lens[s] == 0 gives out[s] = 0.
+ *
+ *   q             [S][Hq][D]                 dtype
+ *   k_cache       [N][Hkv][bs][D]            dtype
+ *   v_cache       [N][Hkv][D][bs]            dtype
+ *   block_tables  [S][max_blocks_per_seq]    int32; only the first
+ *                 ceil(seq_lens[s] / bs) entries of row s are read (the rest may
+ *                 hold anything, e.g. -1 as in [CY] 核心思想 / Block Table)
+ *   seq_lens      [S]                        int32, device memory
+ *   block_size    bs; num_kv_heads Hkv; scale: the logit scale (e.g. 1/sqrt(D))
+ *   out           [S][Hq][D]                 dtype; written, rounded to nearest even
+ *
+ * Arithmetic: fp32 accumulation everywhere.  For f16 / bf16 the softmax weights
+ * are rounded to the input dtype before the weighted sum (matrix-core input).
+ * Long sequences are split into partitions of partition_size tokens; each
+ * partition keeps (running max, running sum, unnormalised output) in the
+ * workspace and a second pass merges them with log-sum-exp weights in a fixed
+ * order, so results are deterministic and do not depend on physical placement.
+ *
+ * Device-side contract (cannot be checked on the host without a sync): table
+ * entries in the used range lie in [0, N) and 0 <= seq_lens[s] <=
+ * max_blocks_per_seq * bs.  A violation never faults: an out-of-range table
+ * entry or length makes every output row of that sequence NaN.
+ *
+ * Workspace: needed when the table can hold more than one partition
+ * (max_blocks_per_seq * bs > partition size); size from pa_decode_workspace_bytes.
+ * Contents need no initialisation.  Calls that share one workspace must be
+ * ordered on one stream.
+ */
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens, int32_t block_size,
+                    int32_t num_kv_heads, float scale, void* out, const pa_decode_ext* ext);
+
+/*
+ * pa_decode_workspace_bytes - bytes of workspace a pa_decode call with these
+ * shapes needs (0 when no sequence can span two partitions).  Only the shape
+ * fields of ext are read.  Returns PA_OK and sets *bytes, or an error status for
+ * the same argument errors pa_decode would report.
+ */
+pa_status pa_decode_workspace_bytes(const pa_decode_ext* ext, int32_t block_size,
+                                    int32_t num_kv_heads, size_t* bytes);
+
+/* Shapes of a pa_cache_write call. */
+typedef struct pa_cache_write_ext {
+  int32_t num_tokens;   /* T >= 0 (0: nothing to do)                 */
+  int32_t num_kv_heads; /* Hkv > 0                                   */
+  int32_t head_dim;     /* D > 0, a multiple of 8                    */
+  int32_t block_size;   /* bs: 4, 8, 16 or 32                        */
+  int64_t num_blocks;   /* N >= 1                                    */
+  int32_t dtype;        /* pa_dtype of k, v and the cache            */
+  void* stream;         /* hipStream_t                               */
+} pa_cache_write_ext;
+
+/*
+ * pa_cache_write - store each new token's key and value in its slot.
+ *
+ * For every token i with slot = slot_mapping[i] >= 0 and every KV head g:
+ *     k_cache[slot / bs][g][slot % bs][:] = k[i][g][:]
+ *     v_cache[slot / bs][g][:][slot % bs] = v[i][g][:]
+ * A token fills the next free slot of its sequence's last block, and a new block
+ * is taken only when that one is full ([RK] 分页注意力是如何工作的; [ASP] 核心思想, a
+ * new block every bs tokens); choosing the slot is the caller's block manager's
+ * job.  A bit copy: the written bytes equal the input bytes.  One launch writes
+ * K and V for all tokens.
+ *
+ *   k, v          [T][Hkv][D]   dtype, device
+ *   slot_mapping  [T]           int64, device; < 0 means "skip this token"
+ *   k_cache, v_cache            as in pa_decode, updated in place
+ *
+ * Device-side contract: slots are unique.  Slots >= N * bs are skipped, never
+ * written.  Do not write into a block that several tables share (such a write
+ * needs copy-on-write first, [CY] 多序列共享; [ASP] 实现要点).
+ */
+pa_status pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
+                         void* k_cache, void* v_cache, const pa_cache_write_ext* ext);
+
+/* Static text for a status code. */
+const char* pa_status_string(pa_status status);
+
+/* Reason for the last non-PA_OK status returned on the calling thread ("" if none).
+ * The pointer stays valid until the next library call on this thread. */
+const char* pa_last_error(void);
+
+/* ABI version of this header: bumped on any incompatible change. */
+int32_t pa_abi_version(void);
+
+#define PA_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,3 +1,7 @@
-"""MI355X-native paged decode attention: a C-ABI library (``libpa.so``) with gfx950 HIP
-kernels, and this thin ctypes binding.  Importing the package does not load the
-library; the first call does, and fails loudly when it is missing."""
+"""MI355X-native paged decode attention: a C-ABI library (``libpa.so``, gfx950 HIP
+kernels) and a thin ctypes binding with the same entry-point names.
+
+Importing the package does not load the library; the first call does, and fails
+loudly when it has not been built."""
+from .binding import (PaError, pa_cache_write, pa_decode,  # noqa: F401
+                      pa_decode_workspace_bytes)

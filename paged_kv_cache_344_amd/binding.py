@@ -1,0 +1,186 @@
+"""ctypes binding for libpa.so: the C entry points under the same names, taking torch
+tensors.  Argument marshalling only -- shapes, dtypes and device placement are checked
+here, pointers and the current HIP stream are handed to the library, and every step
+of the computation runs in the library's kernels.  There is no fallback: if the
+library is missing or a call fails, an exception says so."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+from .build import LIB_PATH, INCLUDE
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_F32, PA_F16, PA_BF16 = range(3)
+TORCH_DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+class DecodeExt(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int64), ("partition_size", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p)]
+
+
+class CacheWriteExt(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("stream", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libpa.so (built in-tree by ``build.build()``); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run paged_kv_cache_344_amd/build.py "
+                               "(or __graft_entry__.build()) first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp,
+                                ctypes.POINTER(DecodeExt)]
+        L.pa_decode.restype = ctypes.c_int
+        L.pa_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeExt), i32, i32,
+                                                ctypes.POINTER(ctypes.c_size_t)]
+        L.pa_decode_workspace_bytes.restype = ctypes.c_int
+        L.pa_cache_write.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(CacheWriteExt)]
+        L.pa_cache_write.restype = ctypes.c_int
+        L.pa_status_string.argtypes = [ctypes.c_int]
+        L.pa_status_string.restype = ctypes.c_char_p
+        L.pa_last_error.argtypes = []
+        L.pa_last_error.restype = ctypes.c_char_p
+        L.pa_abi_version.argtypes = []
+        L.pa_abi_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/pa.h declares."""
+    text = open(os.path.join(INCLUDE, "pa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:pa_status|const char\s*\*|int32_t|size_t)\s+(pa_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def _check(status: int, where: str):
+    if status != PA_OK:
+        L = lib()
+        raise PaError(status, where, L.pa_last_error().decode() or L.pa_status_string(status).decode())
+
+
+def _stream_ptr(device: torch.device, stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def decode_ext(q: torch.Tensor, block_tables: torch.Tensor, num_blocks: int,
+               partition_size: int = 0) -> DecodeExt:
+    S, Hq, D = q.shape
+    return DecodeExt(num_seqs=S, num_q_heads=Hq, head_dim=D,
+                     max_blocks_per_seq=block_tables.shape[1], num_blocks=num_blocks,
+                     partition_size=partition_size, dtype=TORCH_DTYPE[q.dtype],
+                     workspace=None, workspace_bytes=0, stream=None)
+
+
+def pa_decode_workspace_bytes(q: torch.Tensor, block_tables: torch.Tensor, num_blocks: int,
+                              block_size: int, num_kv_heads: int,
+                              partition_size: int = 0) -> int:
+    ext = decode_ext(q, block_tables, num_blocks, partition_size)
+    n = ctypes.c_size_t(0)
+    _check(lib().pa_decode_workspace_bytes(ctypes.byref(ext), block_size, num_kv_heads,
+                                           ctypes.byref(n)), "pa_decode_workspace_bytes")
+    return int(n.value)
+
+
+def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+              block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
+              num_kv_heads: int, scale: float, out: torch.Tensor, *,
+              workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
+              stream=None) -> torch.Tensor:
+    """Decode attention over the paged cache (see include/pa.h for the contract).
+
+    q, out [S, Hq, D]; k_cache [N, Hkv, bs, D]; v_cache [N, Hkv, D, bs];
+    block_tables int32 [S, max_blocks]; seq_lens int32 [S].  All on one GPU.
+    ``workspace`` is a byte tensor of at least ``pa_decode_workspace_bytes`` bytes;
+    when omitted, one is allocated for this call."""
+    dev = q.device
+    _need(dev.type == "cuda", "tensors must be on a GPU")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens), ("out", out)):
+        _need(t.device == dev, f"{name} is on {t.device}, q on {dev}")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(q.dtype in TORCH_DTYPE, f"unsupported dtype {q.dtype}")
+    _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype and out.dtype == q.dtype,
+          "q, k_cache, v_cache and out must share one dtype")
+    _need(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32,
+          "block_tables and seq_lens must be int32")
+    S, Hq, D = q.shape
+    N = k_cache.shape[0]
+    _need(k_cache.shape == (N, num_kv_heads, block_size, D), f"k_cache shape {tuple(k_cache.shape)}")
+    _need(v_cache.shape == (N, num_kv_heads, D, block_size), f"v_cache shape {tuple(v_cache.shape)}")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == S, "block_tables shape")
+    _need(seq_lens.shape == (S,), "seq_lens shape")
+    _need(out.shape == q.shape, "out shape")
+    ext = decode_ext(q, block_tables, N, partition_size)
+    need = ctypes.c_size_t(0)
+    _check(lib().pa_decode_workspace_bytes(ctypes.byref(ext), block_size, num_kv_heads,
+                                           ctypes.byref(need)), "pa_decode")
+    if need.value:
+        if workspace is None:
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+        _need(workspace.device == dev and workspace.is_contiguous(), "workspace placement")
+        ext.workspace = workspace.data_ptr()
+        ext.workspace_bytes = workspace.numel() * workspace.element_size()
+    ext.stream = _stream_ptr(dev, stream)
+    _check(lib().pa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                           block_tables.data_ptr(), seq_lens.data_ptr(), block_size,
+                           num_kv_heads, float(scale), out.data_ptr(), ctypes.byref(ext)),
+           "pa_decode")
+    return out
+
+
+def pa_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, *, stream=None) -> None:
+    """Store new tokens' K/V in their slots (see include/pa.h).  k, v [T, Hkv, D];
+    slot_mapping int64 [T]; caches as for pa_decode."""
+    dev = k.device
+    _need(dev.type == "cuda", "tensors must be on a GPU")
+    for name, t in (("k", k), ("v", v), ("slot_mapping", slot_mapping), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        _need(t.device == dev, f"{name} is on {t.device}, k on {dev}")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(k.dtype in TORCH_DTYPE, f"unsupported dtype {k.dtype}")
+    _need(v.dtype == k.dtype and k_cache.dtype == k.dtype and v_cache.dtype == k.dtype,
+          "k, v and the caches must share one dtype")
+    _need(slot_mapping.dtype == torch.int64, "slot_mapping must be int64")
+    T, Hkv, D = k.shape
+    N, _, bs, _ = k_cache.shape
+    _need(v.shape == k.shape and slot_mapping.shape == (T,), "k / v / slot_mapping shapes")
+    _need(k_cache.shape == (N, Hkv, bs, D) and v_cache.shape == (N, Hkv, D, bs), "cache shapes")
+    ext = CacheWriteExt(num_tokens=T, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                        num_blocks=N, dtype=TORCH_DTYPE[k.dtype],
+                        stream=_stream_ptr(dev, stream))
+    _check(lib().pa_cache_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                                k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(ext)),
+           "pa_cache_write")

@@ -1,0 +1,132 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every
+function include/pa.h declares, and rejects bad arguments with the documented status
+before any HIP call (so fake, never-dereferenced pointers are safe here)."""
+import ctypes
+
+import pytest
+
+from paged_kv_cache_344_amd import binding as B
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = B.header_functions()
+    assert {"pa_decode", "pa_cache_write", "pa_decode_workspace_bytes", "pa_status_string",
+            "pa_last_error", "pa_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.pa_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert lib.pa_status_string(st)
+    assert lib.pa_status_string(99) == b"unknown status"
+
+
+def _ext(**kw):
+    base = dict(num_seqs=8, num_q_heads=32, head_dim=128, max_blocks_per_seq=8192,
+                num_blocks=45056, partition_size=512, dtype=B.PA_BF16, workspace=None,
+                workspace_bytes=0, stream=None)
+    base.update(kw)
+    return B.DecodeExt(**base)
+
+
+def _decode(lib, ext, bs=16, hkv=8, scale=0.088, ptr=FAKE, ext_ptr=True):
+    return lib.pa_decode(ptr, ptr, ptr, ptr, ptr, bs, hkv, ctypes.c_float(scale), ptr,
+                         ctypes.byref(ext) if ext_ptr else None)
+
+
+def _ws(lib, ext, bs=16, hkv=8):
+    n = ctypes.c_size_t(0)
+    st = lib.pa_decode_workspace_bytes(ctypes.byref(ext), bs, hkv, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_formula(lib):
+    # 8 seqs x 32 heads x 256 partitions x (128 + 2) floats, each part 256-byte aligned
+    st, n = _ws(lib, _ext())
+    rows = 8 * 32 * 256
+    assert st == B.PA_OK and n == rows * 128 * 4 + rows * 2 * 4
+    st, n = _ws(lib, _ext(partition_size=-1))          # never split
+    assert st == B.PA_OK and n == 0
+    st, n = _ws(lib, _ext(max_blocks_per_seq=32))      # 512 tokens fit one partition
+    assert st == B.PA_OK and n == 0
+    st, n = _ws(lib, _ext(partition_size=0))           # default is 512 tokens
+    assert st == B.PA_OK and n == rows * 130 * 4
+
+
+@pytest.mark.parametrize("kw,bs,hkv,want", [
+    (dict(num_q_heads=30), 16, 8, B.PA_ERR_INVALID_ARG),      # Hq % Hkv != 0
+    (dict(head_dim=96), 16, 8, B.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=0), 16, 8, B.PA_ERR_INVALID_ARG),
+    (dict(), 64, 8, B.PA_ERR_UNSUPPORTED),                     # block size not built
+    (dict(), 0, 8, B.PA_ERR_INVALID_ARG),
+    (dict(), 16, 0, B.PA_ERR_INVALID_ARG),
+    (dict(dtype=7), 16, 8, B.PA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), 16, 8, B.PA_ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=0), 16, 8, B.PA_ERR_INVALID_ARG),
+    (dict(num_seqs=-1), 16, 8, B.PA_ERR_INVALID_ARG),
+    (dict(num_seqs=70000), 16, 8, B.PA_ERR_INVALID_ARG),
+    (dict(partition_size=100), 16, 8, B.PA_ERR_INVALID_ARG),  # not a multiple of 32
+    (dict(partition_size=32, max_blocks_per_seq=1 << 20), 16, 8, B.PA_ERR_UNSUPPORTED),
+    (dict(), 16, 8, B.PA_ERR_WORKSPACE),                       # split needs a workspace
+    (dict(workspace=FAKE, workspace_bytes=1024), 16, 8, B.PA_ERR_WORKSPACE),
+])
+def test_decode_rejects(lib, kw, bs, hkv, want):
+    st = _decode(lib, _ext(**kw), bs=bs, hkv=hkv)
+    assert st == want, lib.pa_last_error()
+    assert lib.pa_last_error()  # a reason is given
+
+
+def test_decode_rejects_null_and_misaligned(lib):
+    assert _decode(lib, _ext(), ext_ptr=False) == B.PA_ERR_INVALID_ARG
+    assert _decode(lib, _ext(partition_size=-1), ptr=0) == B.PA_ERR_INVALID_ARG
+    assert _decode(lib, _ext(partition_size=-1), ptr=FAKE + 4) == B.PA_ERR_INVALID_ARG
+    assert _decode(lib, _ext(partition_size=-1), scale=float("nan")) == B.PA_ERR_INVALID_ARG
+    assert _decode(lib, _ext(partition_size=-1), scale=float("inf")) == B.PA_ERR_INVALID_ARG
+    # an empty batch is a no-op that touches nothing
+    assert _decode(lib, _ext(num_seqs=0), ptr=0) == B.PA_OK
+
+
+def _cw(lib, ptr=FAKE, slot_ptr=None, **kw):
+    base = dict(num_tokens=128, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=100,
+                dtype=B.PA_BF16, stream=None)
+    base.update(kw)
+    ext = B.CacheWriteExt(**base)
+    sp = ptr if slot_ptr is None else slot_ptr
+    return lib.pa_cache_write(ptr, ptr, sp, ptr, ptr, ctypes.byref(ext))
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(num_tokens=-1), B.PA_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), B.PA_ERR_INVALID_ARG),
+    (dict(head_dim=100), B.PA_ERR_INVALID_ARG),
+    (dict(block_size=12), B.PA_ERR_UNSUPPORTED),
+    (dict(block_size=0), B.PA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), B.PA_ERR_INVALID_ARG),
+    (dict(dtype=3), B.PA_ERR_INVALID_ARG),
+])
+def test_cache_write_rejects(lib, kw, want):
+    assert _cw(lib, **kw) == want
+    assert lib.pa_last_error()
+
+
+def test_cache_write_pointer_checks(lib):
+    assert _cw(lib, ptr=0) == B.PA_ERR_INVALID_ARG
+    assert _cw(lib, ptr=FAKE + 8) == B.PA_ERR_INVALID_ARG
+    assert _cw(lib, slot_ptr=FAKE + 4) == B.PA_ERR_INVALID_ARG
+    assert lib.pa_cache_write(FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.PA_ERR_INVALID_ARG
+    assert _cw(lib, ptr=0, num_tokens=0) == B.PA_OK   # nothing to write
+
+
+def test_last_error_clears_on_success(lib):
+    assert _cw(lib, num_blocks=0) != B.PA_OK and lib.pa_last_error()
+    assert _cw(lib, ptr=0, num_tokens=0) == B.PA_OK
+    assert lib.pa_last_error() == b""
