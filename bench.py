@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode hot path on one MI355X.
+
+One step = one decode step of a batch: ``pa_cache_write`` of the batch's new tokens
+(one per sequence) followed by ``pa_decode`` over every sequence.  The headline batch
+is the bf16 GQA-8 batch (128 sequences, 64 query / 8 KV heads, head dim 128, block
+size 16, log-uniform lengths in [1, 4096], seed 0).  Inputs are resident in HBM before
+timing starts; several copies of the batch are rotated so that no step finds its K/V
+in L2 or the 256 MB Infinity Cache (each copy is 385 MB, four copies 1.5 GB).
+
+Reported (one JSON line on stdout):
+  value      attended KV tokens per second over the whole timed region (K steps,
+             host clock, synchronised on both sides)
+  roofline   the decode call timed with HIP events on the stream it runs on, inside
+             the same timed region: algorithmic bytes per call / mean call duration,
+             against 8 TB/s
+  cpu_baseline  the fp64 oracle on the host cores, on the same batch
+  parity     GPU output of the last timed step against the oracle
+  also       the same decode-only measurement for the long-context batches
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attended KV tokens/s and achieved HBM GB/s (% of peak), decode, 1 MI355X"
+PEAK_GBPS = 8000.0  # MI355X HBM3E peak
+MALL_BYTES = 256 << 20
+HEADLINE = "gqa_bf16"
+WORKLOAD_TEXT = {
+    "gqa_bf16": "bf16 GQA decode step: 128 seqs, 64 q heads / 8 KV heads, head_dim 128, "
+                "block_size 16, log-uniform lengths in [1, 4096], shuffled pool (+10% free); "
+                "pa_cache_write of 128 new tokens, then pa_decode",
+    "long_bf16_bs16": "bf16 long-context split-K decode: 8 seqs, lengths uniform in "
+                      "[32768, 131072], 32 q / 8 KV heads, head_dim 128, block_size 16, "
+                      "512-token partitions",
+    "long_bf16_bs32": "bf16 long-context split-K decode: 8 seqs, lengths uniform in "
+                      "[32768, 131072], 32 q / 8 KV heads, head_dim 128, block_size 32, "
+                      "512-token partitions",
+    "mha_fp16": "fp16 MHA decode: 32 seqs, 32 heads, head_dim 128, block_size 16, "
+                "lengths uniform in [128, 2048]",
+    "prefix_bf16": "bf16 prefix-sharing decode: 64 seqs sharing a 1024-token prefix, "
+                   "0-512 private tokens, 32 q / 8 KV heads, head_dim 128, block_size 16",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def elem_bytes(dtype):
+    return 4 if dtype == "f32" else 2
+
+
+def decode_bytes(b, unique_shared=True):
+    """Algorithmic bytes of one pa_decode call: every attended (token, KV head) K and V
+    row read once (a block shared by several tables counted once when unique_shared),
+    Q read and the output written once, the used table entries and lengths read."""
+    import numpy as np
+    e = elem_bytes(b.dtype)
+    row = b.num_kv_heads * b.head_dim * e * 2
+    tokens = b.total_tokens()
+    if unique_shared and b.shared_blocks:
+        shared_tok = b.shared_blocks * b.block_size
+        tokens = shared_tok + int((b.seq_lens.astype(np.int64) - shared_tok).sum())
+    nb = int(((b.seq_lens.astype(np.int64) + b.block_size - 1) // b.block_size).sum())
+    return tokens * row + 2 * b.num_seqs * b.num_q_heads * b.head_dim * e + 4 * nb + 4 * b.num_seqs
+
+
+def cache_write_bytes(b):
+    if b.slot_mapping is None:
+        return 0
+    T = b.slot_mapping.shape[0]
+    return 2 * (2 * T * b.num_kv_heads * b.head_dim * elem_bytes(b.dtype)) + 8 * T
+
+
+class Copy:
+    """One GPU-resident copy of a batch with its calls prepared."""
+
+    def __init__(self, b, partition_size):
+        import torch
+        import paged_kv_cache_344_amd as pa
+        from paged_kv_cache_344_amd.inputs import as_torch
+        dev = "cuda:0"
+        t = lambda a: as_torch(a, b.dtype, dev)  # noqa: E731
+        self.q, self.kc, self.vc = t(b.q), t(b.k_cache), t(b.v_cache)
+        self.bt = torch.from_numpy(b.block_tables).to(dev)
+        self.sl = torch.from_numpy(b.seq_lens).to(dev)
+        self.out = torch.empty_like(self.q)
+        self.decode = pa.PreparedDecode(self.q, self.kc, self.vc, self.bt, self.sl, b.block_size,
+                                        b.num_kv_heads, b.scale, self.out,
+                                        partition_size=partition_size)
+        self.write = None
+        if b.slot_mapping is not None:
+            self.kn, self.vn = t(b.k_new), t(b.v_new)
+            self.sm = torch.from_numpy(b.slot_mapping).to(dev)
+            self.write = pa.PreparedCacheWrite(self.kn, self.vn, self.sm, self.kc, self.vc)
+
+
+def time_steps(copies, steps, warmup, with_write):
+    """Run warmup + timed steps rotating over copies; returns (elapsed_s, [decode_ms])."""
+    import torch
+    n = len(copies)
+    for k in range(warmup):
+        c = copies[k % n]
+        if with_write and c.write:
+            c.write()
+        c.decode()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        c = copies[k % n]
+        if with_write and c.write:
+            c.write()
+        ev[k][0].record()
+        c.decode()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    return elapsed, [a.elapsed_time(z) for a, z in ev]
+
+
+def oracle_reference(b):
+    """Oracle output for the batch after its cache write, and the host pools."""
+    import oracle
+    kc, vc = b.k_cache.copy(), b.v_cache.copy()
+    if b.slot_mapping is not None:
+        oracle.cache_write(b.k_new, b.v_new, b.slot_mapping, kc, vc, b.block_size, b.dtype)
+    return kc, vc
+
+
+def cpu_baseline(b, kc, vc, budget_s):
+    """The oracle (unchanged) decoding the whole batch on the host cores, repeated
+    until about budget_s seconds have passed (at least once)."""
+    import oracle
+    threads = oracle.set_threads(0)
+    runs, t0, ref = 0, time.perf_counter(), None
+    while True:
+        ref = oracle.decode(b.q, kc, vc, b.block_tables, b.seq_lens, b.block_size,
+                            b.num_kv_heads, b.scale, b.dtype)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / runs * (runs + 1) > 3 * budget_s:
+            break
+    return ref, dict(value=runs * b.total_tokens() / el, unit="tokens/s", cores=threads,
+                     kind="oracle",
+                     sample=f"the whole {b.name} batch (seed {b.seed}, {b.num_seqs} seqs, "
+                            f"sum L = {b.total_tokens()}), after its cache write, decoded "
+                            f"{runs} time(s) in {el:.1f} s by the fp64 C oracle with "
+                            f"{threads} OpenMP threads")
+
+
+def parity(out, ref, dtype):
+    """Same rule as the parity tests: fp32 |d| <= 1e-5 + 1e-5 |ref|; fp16/bf16 |d| <= 1e-2,
+    or one output ulp where half an ulp at |ref| already exceeds 1e-2."""
+    import numpy as np
+    got = out.double().cpu().numpy()
+    d = np.abs(got - ref)
+    if dtype == "f32":
+        tol = 1e-5 + 1e-5 * np.abs(ref)
+    else:
+        mant, emin = (10, -14) if dtype == "f16" else (7, -126)
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** emin))) - mant)
+        tol = np.where(0.5 * ulp > 1e-2, ulp, 1e-2)
+    finite = bool(np.isfinite(got).all())
+    return dict(max_abs=float(d.max()), rule="fp16/bf16: 1e-2 abs (1 ulp above 4 in bf16)"
+                if dtype != "f32" else "fp32: 1e-5 abs + 1e-5 rel",
+                finite=finite, ok=bool(finite and (d <= tol).all()))
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "cache_write.hip", "kernels.h"):
+        h.update(open(os.path.join(ROOT, "paged_kv_cache_344_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, launches_bytes):
+    """HBM bytes per decode call from the committed rocprofv3 counter summary, or None
+    if there is none for the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel_key)
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("bytes_per_call")
+
+
+def measure(name, seed, steps, warmup, copies_min, with_write):
+    import torch
+    from paged_kv_cache_344_amd import inputs
+    t = time.perf_counter()
+    b = inputs.make_batch(name, seed=seed)
+    pool = b.k_cache.nbytes + b.v_cache.nbytes
+    n_copies = max(copies_min, math.ceil(4 * MALL_BYTES / pool)) if pool < 4 * MALL_BYTES else 1
+    log(f"{name}: generated in {time.perf_counter() - t:.1f}s, sum L {b.total_tokens()}, "
+        f"pool {pool / 1e6:.0f} MB, {n_copies} GPU copies")
+    part = b.partition_size
+    copies = [Copy(b, part) for _ in range(n_copies)]
+    torch.cuda.synchronize()
+    elapsed, dms = time_steps(copies, steps, warmup, with_write)
+    dec_bytes = decode_bytes(b)
+    mean_ms = sum(dms) / len(dms)
+    srt = sorted(dms)
+    res = dict(batch=b, copies=copies, elapsed=elapsed, decode_ms=mean_ms,
+               decode_ms_p10=srt[len(srt) // 10], decode_ms_p90=srt[(9 * len(srt)) // 10],
+               decode_bytes=dec_bytes, write_bytes=cache_write_bytes(b) if with_write else 0,
+               gbps=dec_bytes / (mean_ms * 1e-3) / 1e9, n_copies=n_copies)
+    log(f"{name}: {steps} steps in {elapsed * 1e3:.2f} ms; decode call {mean_ms * 1e3:.1f} us "
+        f"(p10 {res['decode_ms_p10'] * 1e3:.1f}, p90 {res['decode_ms_p90'] * 1e3:.1f}); "
+        f"{res['gbps']:.0f} GB/s = {res['gbps'] / PEAK_GBPS:.1%} of peak")
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=4, help="minimum rotated copies of a batch")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--also", default="long_bf16_bs16,long_bf16_bs32",
+                    help="comma-separated secondary batches measured decode-only ('' for none)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this library "
+              "runs its hot path on a single MI355X; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    from paged_kv_cache_344_amd.binding import lib
+    lib()
+
+    head = measure(HEADLINE, args.seed, args.steps, args.warmup, args.copies, with_write=True)
+    b = head["batch"]
+    tokens = b.total_tokens()
+    value = args.steps * tokens / head["elapsed"]
+
+    kc, vc = oracle_reference(b)
+    if args.no_cpu_baseline:
+        import oracle
+        ref = oracle.decode(b.q, kc, vc, b.block_tables, b.seq_lens, b.block_size,
+                            b.num_kv_heads, b.scale, b.dtype)
+        cpu = None
+    else:
+        ref, cpu = cpu_baseline(b, kc, vc, args.cpu_seconds)
+        log(f"cpu baseline: {cpu['value']:.3g} tokens/s on {cpu['cores']} threads")
+    last = head["copies"][(args.steps - 1) % head["n_copies"]]
+    par = parity(last.out, ref, b.dtype)
+    log(f"parity: {par}")
+
+    also = {}
+    for name in [x for x in args.also.split(",") if x]:
+        r = measure(name, args.seed, max(20, args.steps // 4), args.warmup, 1, with_write=False)
+        rb = r["batch"]
+        also[name] = dict(workload=WORKLOAD_TEXT.get(name, name), sum_L=rb.total_tokens(),
+                          tokens_per_s=rb.total_tokens() / (r["decode_ms"] * 1e-3),
+                          decode_us=r["decode_ms"] * 1e3, decode_us_p10=r["decode_ms_p10"] * 1e3,
+                          decode_us_p90=r["decode_ms_p90"] * 1e3,
+                          algorithmic_bytes=r["decode_bytes"], achieved_gbps=r["gbps"],
+                          frac_of_peak=r["gbps"] / PEAK_GBPS)
+        del r
+        torch.cuda.empty_cache()
+
+    traffic = measured_traffic(f"{HEADLINE}/pa_decode", head["decode_bytes"])
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["elapsed"] / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[HEADLINE], "batch": HEADLINE, "seed": args.seed,
+                   "num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads,
+                   "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
+                   "block_size": b.block_size, "sum_L": tokens,
+                   "partition_size": b.partition_size or 512,
+                   "rotated_copies": head["n_copies"], "parallelism": "1 GPU"},
+        "roofline": {"bound": "hbm", "achieved": head["gbps"], "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": head["gbps"] / PEAK_GBPS, "traffic": traffic,
+                     "kernel": "pa_decode call (partition kernel + split-K merge kernel)",
+                     "algorithmic_bytes_per_call": head["decode_bytes"],
+                     "mean_call_us": head["decode_ms"] * 1e3,
+                     "p10_call_us": head["decode_ms_p10"] * 1e3,
+                     "p90_call_us": head["decode_ms_p90"] * 1e3},
+        "cpu_baseline": cpu,
+        "parity": par,
+        "step_bytes": head["decode_bytes"] + head["write_bytes"],
+        "also": also,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

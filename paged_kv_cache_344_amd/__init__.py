@@ -3,5 +3,5 @@ kernels) and a thin ctypes binding with the same entry-point names.
 
 Importing the package does not load the library; the first call does, and fails
 loudly when it has not been built."""
-from .binding import (PaError, pa_cache_write, pa_decode,  # noqa: F401
-                      pa_decode_workspace_bytes)
+from .binding import (PaError, PreparedCacheWrite, PreparedDecode,  # noqa: F401
+                      pa_cache_write, pa_decode, pa_decode_workspace_bytes)

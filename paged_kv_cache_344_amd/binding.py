@@ -113,6 +113,62 @@ def pa_decode_workspace_bytes(q: torch.Tensor, block_tables: torch.Tensor, num_b
     return int(n.value)
 
 
+class PreparedDecode:
+    """A pa_decode call with all marshalling done once; calling the object issues the
+    single C call (no Python-side checks or allocation), e.g. inside a timed loop or
+    HIP graph capture.  Keeps references to every tensor it points at."""
+
+    def __init__(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
+                 num_kv_heads: int, scale: float, out: torch.Tensor, *,
+                 workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
+                 stream=None):
+        dev = q.device
+        _need(dev.type == "cuda", "tensors must be on a GPU")
+        for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                        ("block_tables", block_tables), ("seq_lens", seq_lens), ("out", out)):
+            _need(t.device == dev, f"{name} is on {t.device}, q on {dev}")
+            _need(t.is_contiguous(), f"{name} must be contiguous")
+        _need(q.dtype in TORCH_DTYPE, f"unsupported dtype {q.dtype}")
+        _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype and out.dtype == q.dtype,
+              "q, k_cache, v_cache and out must share one dtype")
+        _need(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32,
+              "block_tables and seq_lens must be int32")
+        S, Hq, D = q.shape
+        N = k_cache.shape[0]
+        _need(k_cache.shape == (N, num_kv_heads, block_size, D),
+              f"k_cache shape {tuple(k_cache.shape)}")
+        _need(v_cache.shape == (N, num_kv_heads, D, block_size),
+              f"v_cache shape {tuple(v_cache.shape)}")
+        _need(block_tables.dim() == 2 and block_tables.shape[0] == S, "block_tables shape")
+        _need(seq_lens.shape == (S,), "seq_lens shape")
+        _need(out.shape == q.shape, "out shape")
+        ext = decode_ext(q, block_tables, N, partition_size)
+        need = ctypes.c_size_t(0)
+        _check(lib().pa_decode_workspace_bytes(ctypes.byref(ext), block_size, num_kv_heads,
+                                               ctypes.byref(need)), "pa_decode")
+        if need.value:
+            if workspace is None:
+                workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+            _need(workspace.device == dev and workspace.is_contiguous(), "workspace placement")
+            ext.workspace = workspace.data_ptr()
+            ext.workspace_bytes = workspace.numel() * workspace.element_size()
+        ext.stream = _stream_ptr(dev, stream)
+        self.ext = ext
+        self.tensors = (q, k_cache, v_cache, block_tables, seq_lens, out, workspace)
+        self.out = out
+        self._fn = lib().pa_decode
+        self._args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                      block_tables.data_ptr(), seq_lens.data_ptr(), block_size, num_kv_heads,
+                      ctypes.c_float(scale), out.data_ptr(), ctypes.byref(ext))
+
+    def __call__(self) -> torch.Tensor:
+        st = self._fn(*self._args)
+        if st != PA_OK:
+            _check(st, "pa_decode")
+        return self.out
+
+
 def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
               num_kv_heads: int, scale: float, out: torch.Tensor, *,
@@ -124,63 +180,47 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     block_tables int32 [S, max_blocks]; seq_lens int32 [S].  All on one GPU.
     ``workspace`` is a byte tensor of at least ``pa_decode_workspace_bytes`` bytes;
     when omitted, one is allocated for this call."""
-    dev = q.device
-    _need(dev.type == "cuda", "tensors must be on a GPU")
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
-                    ("block_tables", block_tables), ("seq_lens", seq_lens), ("out", out)):
-        _need(t.device == dev, f"{name} is on {t.device}, q on {dev}")
-        _need(t.is_contiguous(), f"{name} must be contiguous")
-    _need(q.dtype in TORCH_DTYPE, f"unsupported dtype {q.dtype}")
-    _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype and out.dtype == q.dtype,
-          "q, k_cache, v_cache and out must share one dtype")
-    _need(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32,
-          "block_tables and seq_lens must be int32")
-    S, Hq, D = q.shape
-    N = k_cache.shape[0]
-    _need(k_cache.shape == (N, num_kv_heads, block_size, D), f"k_cache shape {tuple(k_cache.shape)}")
-    _need(v_cache.shape == (N, num_kv_heads, D, block_size), f"v_cache shape {tuple(v_cache.shape)}")
-    _need(block_tables.dim() == 2 and block_tables.shape[0] == S, "block_tables shape")
-    _need(seq_lens.shape == (S,), "seq_lens shape")
-    _need(out.shape == q.shape, "out shape")
-    ext = decode_ext(q, block_tables, N, partition_size)
-    need = ctypes.c_size_t(0)
-    _check(lib().pa_decode_workspace_bytes(ctypes.byref(ext), block_size, num_kv_heads,
-                                           ctypes.byref(need)), "pa_decode")
-    if need.value:
-        if workspace is None:
-            workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
-        _need(workspace.device == dev and workspace.is_contiguous(), "workspace placement")
-        ext.workspace = workspace.data_ptr()
-        ext.workspace_bytes = workspace.numel() * workspace.element_size()
-    ext.stream = _stream_ptr(dev, stream)
-    _check(lib().pa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                           block_tables.data_ptr(), seq_lens.data_ptr(), block_size,
-                           num_kv_heads, float(scale), out.data_ptr(), ctypes.byref(ext)),
-           "pa_decode")
-    return out
+    return PreparedDecode(q, k_cache, v_cache, block_tables, seq_lens, block_size,
+                          num_kv_heads, scale, out, workspace=workspace,
+                          partition_size=partition_size, stream=stream)()
+
+
+class PreparedCacheWrite:
+    """A pa_cache_write call with all marshalling done once (see PreparedDecode)."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                 k_cache: torch.Tensor, v_cache: torch.Tensor, *, stream=None):
+        dev = k.device
+        _need(dev.type == "cuda", "tensors must be on a GPU")
+        for name, t in (("k", k), ("v", v), ("slot_mapping", slot_mapping),
+                        ("k_cache", k_cache), ("v_cache", v_cache)):
+            _need(t.device == dev, f"{name} is on {t.device}, k on {dev}")
+            _need(t.is_contiguous(), f"{name} must be contiguous")
+        _need(k.dtype in TORCH_DTYPE, f"unsupported dtype {k.dtype}")
+        _need(v.dtype == k.dtype and k_cache.dtype == k.dtype and v_cache.dtype == k.dtype,
+              "k, v and the caches must share one dtype")
+        _need(slot_mapping.dtype == torch.int64, "slot_mapping must be int64")
+        T, Hkv, D = k.shape
+        N, _, bs, _ = k_cache.shape
+        _need(v.shape == k.shape and slot_mapping.shape == (T,), "k / v / slot_mapping shapes")
+        _need(k_cache.shape == (N, Hkv, bs, D) and v_cache.shape == (N, Hkv, D, bs),
+              "cache shapes")
+        self.ext = CacheWriteExt(num_tokens=T, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                                 num_blocks=N, dtype=TORCH_DTYPE[k.dtype],
+                                 stream=_stream_ptr(dev, stream))
+        self.tensors = (k, v, slot_mapping, k_cache, v_cache)
+        self._fn = lib().pa_cache_write
+        self._args = (k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
+                      v_cache.data_ptr(), ctypes.byref(self.ext))
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != PA_OK:
+            _check(st, "pa_cache_write")
 
 
 def pa_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                    k_cache: torch.Tensor, v_cache: torch.Tensor, *, stream=None) -> None:
     """Store new tokens' K/V in their slots (see include/pa.h).  k, v [T, Hkv, D];
     slot_mapping int64 [T]; caches as for pa_decode."""
-    dev = k.device
-    _need(dev.type == "cuda", "tensors must be on a GPU")
-    for name, t in (("k", k), ("v", v), ("slot_mapping", slot_mapping), ("k_cache", k_cache),
-                    ("v_cache", v_cache)):
-        _need(t.device == dev, f"{name} is on {t.device}, k on {dev}")
-        _need(t.is_contiguous(), f"{name} must be contiguous")
-    _need(k.dtype in TORCH_DTYPE, f"unsupported dtype {k.dtype}")
-    _need(v.dtype == k.dtype and k_cache.dtype == k.dtype and v_cache.dtype == k.dtype,
-          "k, v and the caches must share one dtype")
-    _need(slot_mapping.dtype == torch.int64, "slot_mapping must be int64")
-    T, Hkv, D = k.shape
-    N, _, bs, _ = k_cache.shape
-    _need(v.shape == k.shape and slot_mapping.shape == (T,), "k / v / slot_mapping shapes")
-    _need(k_cache.shape == (N, Hkv, bs, D) and v_cache.shape == (N, Hkv, D, bs), "cache shapes")
-    ext = CacheWriteExt(num_tokens=T, num_kv_heads=Hkv, head_dim=D, block_size=bs,
-                        num_blocks=N, dtype=TORCH_DTYPE[k.dtype],
-                        stream=_stream_ptr(dev, stream))
-    _check(lib().pa_cache_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
-                                k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(ext)),
-           "pa_cache_write")
+    PreparedCacheWrite(k, v, slot_mapping, k_cache, v_cache, stream=stream)()

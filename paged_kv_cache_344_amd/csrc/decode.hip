@@ -36,6 +36,10 @@
 // sequence end are removed by select (never by multiplying: the unused slots of
 // the last block may hold anything, and 0 * NaN = NaN).
 //
+// Precision.  Inputs are exact in the MFMA; products accumulate in fp32.  The
+// softmax weights enter the weighted sum as a bf16/f16 hi + lo pair (two MFMAs),
+// which keeps them to about fp32 accuracy.
+//
 // Split-K.  A partition with p > 0 or a sequence with more than one partition
 // writes (max, sum, unnormalised output) to the workspace; decode_merge_kernel
 // combines them with log-sum-exp weights in partition order.  Sequences that fit
@@ -302,12 +306,23 @@ __global__ __launch_bounds__(NW * 64) void decode_partitions_kernel(DecodeParams
       }
     }
     if constexpr (sizeof(T) == 2) {
+      // weights as hi + lo pairs of the input type: the sum of two products keeps
+      // ~16 significant bits of each fp32 weight, so the weighted sum is as exact as
+      // an fp32 one and the only rounding left is the final store
       typedef typename Vec8<T>::type V8;
-      V8 pv;
+      V8 phi, plo;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = (T)pr[e];
+      for (int e = 0; e < 8; ++e) {
+        const T h = (T)pr[e];
+        phi[e] = h;
+        plo[e] = (T)(pr[e] - (float)h);
+      }
 #pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] = mma16(__builtin_bit_cast(V8, c.v[n][0]), pv, acc[n]);
+      for (int n = 0; n < NT; ++n) {
+        const V8 vv = __builtin_bit_cast(V8, c.v[n][0]);
+        acc[n] = mma16(vv, phi, acc[n]);
+        acc[n] = mma16(vv, plo, acc[n]);
+      }
     } else {
 #pragma unroll
       for (int n = 0; n < NT; ++n) {

@@ -13,9 +13,11 @@ Storage convention of the cache (the library's definition; the pages fix none):
 ``k_cache[N][Hkv][bs][D]`` and ``v_cache[N][Hkv][D][bs]``.  Arrays are returned as
 raw numpy storage: float32, float16, or uint16 bit patterns for bf16.
 
-Draw order for one batch: lengths, block permutation, Q, K pool, V pool, new K,
-new V.  Unused table entries are -1 ([CY] "深入解析 PagedAttention" 核心思想,
-Block Table example).  Every slot no sequence owns (free blocks, the unfilled tail
+Draw order for one batch: lengths, block permutation, Q and the new tokens' K and V
+come from ``default_rng(seed)`` in that order; the K and V pools are filled chunk by
+chunk from child generators of ``SeedSequence(seed)`` (spawn keys 1 and 2), so large
+pools can be drawn on several threads with the same result.  Unused table entries
+are -1 ([CY] "深入解析 PagedAttention" 核心思想, Block Table example).  Every slot no sequence owns (free blocks, the unfilled tail
 of a sequence's last block, and the slot a pending new token will fill) holds NaN,
 so a kernel that touches one shows it.
 
@@ -25,8 +27,10 @@ PagedAttention：vLLM 显存优化的核心魔法" (cygnushan.xyz); [RK] "什么
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -106,6 +110,41 @@ def to_storage(x32: np.ndarray, dtype: str) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
+def _nan(dtype: str):
+    return {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(0x7FC0)}[dtype]
+
+
+_CHUNK_VALUES = 1 << 22
+
+
+def _fill_pool(block_shape, N, seed, key, dtype, owned) -> np.ndarray:
+    """[N, *block_shape] storage: N(0, 1) in owned blocks, NaN elsewhere.  Drawn in
+    chunks of whole blocks, chunk i from child i of SeedSequence(seed, spawn_key=(key,)),
+    so the values do not depend on how many threads fill it."""
+    per_block = int(np.prod(block_shape))
+    chunk = max(1, _CHUNK_VALUES // per_block)
+    n_chunks = (N + chunk - 1) // chunk
+    children = np.random.SeedSequence(entropy=seed, spawn_key=(key,)).spawn(n_chunks)
+    out = np.empty((N,) + tuple(block_shape), dtype=STORAGE[dtype])
+    nan = _nan(dtype)
+
+    def work(i):
+        a, b = i * chunk, min(N, (i + 1) * chunk)
+        x = np.random.default_rng(children[i]).standard_normal((b - a,) + tuple(block_shape),
+                                                              dtype=np.float32)
+        out[a:b] = to_storage(x, dtype)
+        out[a:b][~owned[a:b]] = nan
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    if n_chunks == 1 or threads == 1:
+        for i in range(n_chunks):
+            work(i)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(work, range(n_chunks)))
+    return out
+
+
 def _draw_lengths(rng, spec, S):
     kind = spec[0]
     if kind == "fixed":
@@ -172,21 +211,20 @@ def make_batch(name: str, seed: int = 0, **over) -> Batch:
     q32 = rng.standard_normal((S, Hq, D), dtype=np.float32)
     if q_gain != 1.0:
         q32 *= np.float32(q_gain)
-    k32 = rng.standard_normal((N, Hkv, bs, D), dtype=np.float32)
-    v32 = rng.standard_normal((N, Hkv, D, bs), dtype=np.float32)
 
-    # poison everything no sequence owns
+    # pools: N(0, 1) in every owned block, NaN in every free block
     owned = np.zeros(N, dtype=bool)
     for s in range(S):
         owned[bt[s, :nblk[s]]] = True
-    k32[~owned] = np.nan
-    v32[~owned] = np.nan
-    for s in range(S):
+    k_cache = _fill_pool((Hkv, bs, D), N, seed, 1, dtype, owned)
+    v_cache = _fill_pool((Hkv, D, bs), N, seed, 2, dtype, owned)
+    nan = _nan(dtype)
+    for s in range(S):  # the unfilled tail of each sequence's last block
         L = int(lens[s])
         if L % bs:
             last = bt[s, L // bs]
-            k32[last, :, L % bs:, :] = np.nan
-            v32[last, :, :, L % bs:] = np.nan
+            k_cache[last, :, L % bs:, :] = nan
+            v_cache[last, :, :, L % bs:] = nan
 
     k_new = v_new = slots = None
     if cfg.get("cache_write"):
@@ -197,8 +235,8 @@ def make_batch(name: str, seed: int = 0, **over) -> Batch:
         blk = bt[np.arange(S), pos // bs].astype(np.int64)
         off = pos % bs
         slots = blk * bs + off
-        k32[blk, :, off, :] = np.nan
-        v32[blk, :, :, off] = np.nan
+        k_cache[blk, :, off, :] = nan
+        v_cache[blk, :, :, off] = nan
         kn32 = rng.standard_normal((S, Hkv, D), dtype=np.float32)
         vn32 = rng.standard_normal((S, Hkv, D), dtype=np.float32)
         k_new, v_new = to_storage(kn32, dtype), to_storage(vn32, dtype)
@@ -207,8 +245,8 @@ def make_batch(name: str, seed: int = 0, **over) -> Batch:
     return Batch(name=name, seed=seed, dtype=dtype, num_seqs=S, num_q_heads=Hq,
                  num_kv_heads=Hkv, head_dim=D, block_size=bs, max_blocks_per_seq=MB,
                  num_blocks=N, scale=scale, seq_lens=lens.astype(np.int32), block_tables=bt,
-                 q=to_storage(q32, dtype), k_cache=to_storage(k32, dtype),
-                 v_cache=to_storage(v32, dtype), k_new=k_new, v_new=v_new,
+                 q=to_storage(q32, dtype), k_cache=k_cache, v_cache=v_cache,
+                 k_new=k_new, v_new=v_new,
                  slot_mapping=None if slots is None else slots.astype(np.int64),
                  partition_size=int(cfg.get("partition_size", 0)), shared_blocks=shared)
 

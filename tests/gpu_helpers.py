@@ -80,7 +80,7 @@ def oracle_decode(b: Batch, kc=None, vc=None, seqs=None) -> np.ndarray:
 
 
 def raw_bytes(t: torch.Tensor) -> np.ndarray:
-    return t.detach().contiguous().cpu().view(torch.uint8).numpy()
+    return t.detach().contiguous().cpu().view(torch.uint8).numpy().reshape(-1)
 
 
 def storage_of(t: torch.Tensor, dtype: str) -> np.ndarray:
