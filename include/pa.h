@@ -45,7 +45,7 @@
  *   32; num_q_heads a multiple of num_kv_heads.  Anything else is
  *   PA_ERR_UNSUPPORTED or PA_ERR_INVALID_ARG.
  * - Calls are reentrant and thread-safe: no global mutable state beyond the
- *   thread-local error text.
+ *   thread-local error text and a per-device cache of the decode launch size.
  */
 #ifndef PA_H
 #define PA_H
@@ -61,7 +61,7 @@ typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = 1, /* a null pointer, a bad size, a misaligned pointer       */
   PA_ERR_UNSUPPORTED = 2, /* valid but not built: dtype / head_dim / block_size ... */
-  PA_ERR_WORKSPACE = 3,   /* split-K workspace missing or smaller than required      */
+  PA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required       */
   PA_ERR_HIP = 4          /* the HIP runtime refused a launch; see pa_last_error()   */
 } pa_status;
 
@@ -77,7 +77,8 @@ typedef struct pa_decode_ext {
   int32_t partition_size;     /* tokens per split-K partition: 0 = 512 (default),      */
                               /* < 0 = never split, > 0 = that many (multiple of 32)  */
   int32_t dtype;              /* pa_dtype of q, k_cache, v_cache and out               */
-  void* workspace;            /* device scratch for split-K partials (caller-owned)    */
+  void* workspace;            /* device scratch: queue, counters, split-K partials;    */
+                              /* caller-owned, zero-filled before first use            */
   size_t workspace_bytes;     /* its size; see pa_decode_workspace_bytes               */
   void* stream;               /* hipStream_t                                           */
 } pa_decode_ext;
@@ -110,18 +111,30 @@ typedef struct pa_decode_ext {
  * are rounded to the input dtype before the weighted sum (matrix-core input).
  * Long sequences are split into partitions of partition_size tokens; each
  * partition keeps (running max, running sum, unnormalised output) in the
- * workspace and a second pass merges them with log-sum-exp weights in a fixed
- * order, so results are deterministic and do not depend on physical placement.
+ * workspace, and the partitions are combined with log-sum-exp weights along a
+ * fixed tree (groups of 16 partitions, then the groups) inside the same launch,
+ * so results are deterministic and do not depend on physical placement or on
+ * timing.
  *
  * Device-side contract (cannot be checked on the host without a sync): table
  * entries in the used range lie in [0, N) and 0 <= seq_lens[s] <=
  * max_blocks_per_seq * bs.  A violation never faults: an out-of-range table
  * entry or length makes every output row of that sequence NaN.
  *
- * Workspace: needed when the table can hold more than one partition
- * (max_blocks_per_seq * bs > partition size); size from pa_decode_workspace_bytes.
- * Contents need no initialisation.  Calls that share one workspace must be
- * ordered on one stream.
+ * Workspace (ext->workspace, ext->workspace_bytes): device memory owned by the
+ * caller, of at least pa_decode_workspace_bytes bytes, needed by every call.  It
+ * holds the work queue and merge counters of the launch and, when a sequence can
+ * span several partitions, the per-partition partial results.  It must be
+ * zero-filled before its first use.  Every call that returns PA_OK and runs to
+ * completion returns its counters (the leading part of the workspace, up to the
+ * partial results) to zero; the partial results are scratch that needs no
+ * clearing.  So one workspace serves any number of calls, of any shape it is large
+ * enough for.  Calls that share a workspace must be ordered on one stream: calls
+ * that overlap on the same workspace race.
+ *
+ * Execution: one persistent launch per 1024 sequences (about as many workgroups
+ * as are resident on the device at once), each planning from seq_lens which
+ * partitions hold tokens and taking work items from a queue in the workspace.
  */
 pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* seq_lens, int32_t block_size,
@@ -129,9 +142,12 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
 
 /*
  * pa_decode_workspace_bytes - bytes of workspace a pa_decode call with these
- * shapes needs (0 when no sequence can span two partitions).  Only the shape
- * fields of ext are read.  Returns PA_OK and sets *bytes, or an error status for
- * the same argument errors pa_decode would report.
+ * shapes needs (always > 0: a few hundred bytes of counters when no sequence can
+ * span two partitions, plus S * Hq * pmax * (D + 2) * 4 bytes of partials when
+ * one can, pmax = ceil(max_blocks_per_seq * bs / partition size), and a further
+ * S * Hq * ceil(pmax / 16) * (D + 2) * 4 when pmax > 16).  Only the shape fields of
+ * ext are read.  Returns PA_OK and sets *bytes, or an error status for the same
+ * argument errors pa_decode would report.
  */
 pa_status pa_decode_workspace_bytes(const pa_decode_ext* ext, int32_t block_size,
                                     int32_t num_kv_heads, size_t* bytes);

@@ -94,6 +94,15 @@ def _need(cond: bool, msg: str):
         raise ValueError(msg)
 
 
+def workspace_for(q: torch.Tensor, block_tables: torch.Tensor, num_blocks: int,
+                  block_size: int, num_kv_heads: int, partition_size: int = 0) -> torch.Tensor:
+    """A zero-filled decode workspace for calls of this shape (reusable across calls
+    that are ordered on one stream)."""
+    n = pa_decode_workspace_bytes(q, block_tables, num_blocks, block_size, num_kv_heads,
+                                  partition_size)
+    return torch.zeros(n, dtype=torch.uint8, device=q.device)
+
+
 def decode_ext(q: torch.Tensor, block_tables: torch.Tensor, num_blocks: int,
                partition_size: int = 0) -> DecodeExt:
     S, Hq, D = q.shape
@@ -147,12 +156,13 @@ class PreparedDecode:
         need = ctypes.c_size_t(0)
         _check(lib().pa_decode_workspace_bytes(ctypes.byref(ext), block_size, num_kv_heads,
                                                ctypes.byref(need)), "pa_decode")
-        if need.value:
-            if workspace is None:
-                workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
-            _need(workspace.device == dev and workspace.is_contiguous(), "workspace placement")
-            ext.workspace = workspace.data_ptr()
-            ext.workspace_bytes = workspace.numel() * workspace.element_size()
+        if workspace is None:
+            # zero-filled, as the library requires before a workspace's first use;
+            # every call returns its counters to zero
+            workspace = torch.zeros(need.value, dtype=torch.uint8, device=dev)
+        _need(workspace.device == dev and workspace.is_contiguous(), "workspace placement")
+        ext.workspace = workspace.data_ptr()
+        ext.workspace_bytes = workspace.numel() * workspace.element_size()
         ext.stream = _stream_ptr(dev, stream)
         self.ext = ext
         self.tensors = (q, k_cache, v_cache, block_tables, seq_lens, out, workspace)
@@ -178,8 +188,9 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
     q, out [S, Hq, D]; k_cache [N, Hkv, bs, D]; v_cache [N, Hkv, D, bs];
     block_tables int32 [S, max_blocks]; seq_lens int32 [S].  All on one GPU.
-    ``workspace`` is a byte tensor of at least ``pa_decode_workspace_bytes`` bytes;
-    when omitted, one is allocated for this call."""
+    ``workspace`` is a byte tensor of at least ``pa_decode_workspace_bytes`` bytes,
+    zero-filled before its first use (every call returns its counters to zero, so
+    it can be reused); when omitted, a zero-filled one is allocated for this call."""
     return PreparedDecode(q, k_cache, v_cache, block_tables, seq_lens, block_size,
                           num_kv_heads, scale, out, workspace=workspace,
                           partition_size=partition_size, stream=stream)()

@@ -1,49 +1,64 @@
-// decode.hip - gfx950 kernels behind pa_decode.
+// decode.hip - the gfx950 kernel behind pa_decode.
 //
 // Pages cited (title, site): [AB] "什么是分页注意力（PagedAttention）？" aiboss88.com;
 // [ASP] "PagedAttention" awesome-system-papers; [RK] "什么是 LLM 中的分页注意力(Paged
 // Attention)?它是如何工作的?" news.rkmt.cn.
 //
-// What runs.  One workgroup (4 waves) per (sequence s, KV head g, 16-query-head
-// tile, partition p of the sequence's tokens).  The attention formula is the plain
-// one ([AB] 边界与常见误解: paging does not change it); what paging changes is that
-// every 32-token chunk looks its physical blocks up in the block table and
-// gathers K and V from wherever they sit ([ASP] 实现要点, the kernel that takes a
-// block table; [RK] 块表).  Inside a block the reads stay contiguous ([ASP] 核心思想).
+// What is computed.  For every sequence s and query head h, softmax attention of
+// q[s][h] over the sequence's keys and values in logical order.  Paging leaves
+// that formula alone ([AB] 边界与常见误解); what it changes is where token t lives:
+// in physical block block_tables[s][t / bs] at offset t % bs ([RK] 块表), so the
+// kernel looks each block up in the table and gathers it from wherever it sits
+// ([ASP] 实现要点, the kernel that takes a block table).  Inside a block the reads
+// are contiguous ([ASP] 核心思想).
 //
-// Matrix cores.  The G query heads of one KV head share every K/V byte, so the
-// logits of a 32-token chunk are a (tokens x D) by (D x heads) product and the
-// weighted sum is a (D x tokens) by (tokens x heads) product.  Both run on MFMA
-// 16x16 tiles (16x16x32 for f16/bf16, 16x16x4 for f32) with heads on the N side,
-// padded to 16.  Operand layouts were chosen so that no byte moves between lanes:
-//   * QK: A = K rows (M = 16 tokens, K = head dim), B = q^T.  A lane's A operand is
-//     a 16-byte slice of one key row, loaded straight from HBM.
-//   * The two QK tiles of a chunk take tokens {8i..8i+3} and {8i+4..8i+7} of the
-//     chunk, i = 0..3, so the C layout of the logits leaves lane (head c, quad i)
-//     holding tokens 8i..8i+7 of head c - exactly the B operand (P^T) of the next
-//     product.
+// Work items.  A sequence is cut into partitions of part_tokens tokens; a work item
+// is (sequence, partition, KV head, tile of up to 16 of its query heads) and is
+// handled by one 4-wave workgroup.  The launch is persistent: about as many
+// workgroups as fit on the chip at once, each taking items from a queue counter
+// until none are left.  Lengths live in device memory, so every workgroup first
+// plans for itself, in LDS, from seq_lens: it enumerates only the partitions that
+// hold tokens (no workgroup is spent on partitions past a sequence's end), full
+// partitions first and then each sequence's last, partly filled partition in
+// decreasing size, so that the last items to start are the short ones.  Every
+// workgroup computes the same plan.
+//
+// Inside an item the four waves take 32-token chunks in turn.  The G query heads of
+// one KV head share every K/V byte, so the logits of a chunk are a (tokens x D) by
+// (D x heads) product and the weighted sum is a (D x tokens) by (tokens x heads)
+// product; both run on 16x16 MFMA tiles (16x16x32 for f16/bf16, 16x16x4 for f32)
+// with the heads on the N side, padded to 16.  Operand layouts were chosen so that
+// no byte moves between lanes:
+//   * QK: A = K rows (M = 16 tokens, K = head dim), B = q^T.  A lane's A operand is a
+//     16-byte slice of one key row, loaded straight from HBM.
+//   * The two QK tiles of a chunk take tokens {8i..8i+3} and {8i+4..8i+7} of the chunk,
+//     i = 0..3, so the C layout of the logits leaves lane (head c, quad i) holding
+//     tokens 8i..8i+7 of head c: exactly the B operand (P^T) of the next product.
 //   * PV: A = V^T (M = 16 dims, K = 32 tokens), B = P^T.  The value cache is stored
-//     dimension-major inside a block, so a lane's A operand (8 consecutive tokens
-//     of one dimension) is again one 16-byte load.
-//   * The output O^T (dims x heads) keeps head c in lane column c, the same lane
-//     column that owns head c's running max and sum, so the online-softmax rescale
-//     never crosses lanes.
-// LDS is used only to merge the four waves' partial results at the end.
+//     dimension-major inside a block, so a lane's A operand (8 consecutive tokens of
+//     one dimension) is again one 16-byte load.
+//   * The output O^T (dims x heads) keeps head c in lane column c, the lane column
+//     that owns head c's running max and sum, so the softmax rescale never crosses
+//     lanes.
+// Each wave keeps two chunks' loads in flight (ping-pong register buffers).
 //
 // Softmax.  Online: per chunk, new max m' = max(m, max z), rescale the running sum
 // and output by 2^(m - m'), add 2^(z - m').  Logits are in base-2 units (scale
 // pre-multiplied by log2 e), so each weight is one v_exp_f32.  Positions past the
-// sequence end are removed by select (never by multiplying: the unused slots of
-// the last block may hold anything, and 0 * NaN = NaN).
+// sequence end are removed by select, never by multiplying: the unused slots of the
+// last block may hold anything, and 0 * NaN = NaN.
 //
 // Precision.  Inputs are exact in the MFMA; products accumulate in fp32.  The
 // softmax weights enter the weighted sum as a bf16/f16 hi + lo pair (two MFMAs),
 // which keeps them to about fp32 accuracy.
 //
-// Split-K.  A partition with p > 0 or a sequence with more than one partition
-// writes (max, sum, unnormalised output) to the workspace; decode_merge_kernel
-// combines them with log-sum-exp weights in partition order.  Sequences that fit
-// in one partition are finished by their only workgroup.
+// Split-K merge.  A sequence with one partition is finished by its only item.
+// Otherwise each item stores (max, sum, unnormalised output) per head; partitions
+// form groups of 16, and the item that completes a group (an arrival counter)
+// combines the group with log-sum-exp weights, and the item that completes the
+// last group combines the groups.  The tree is fixed by partition numbers, so the
+// result does not depend on timing or on which workgroup ran what.  Counters are
+// reset by whoever finishes them, so they are all zero again after a call.
 #include <math.h>
 
 #include "kernels.h"
@@ -60,6 +75,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define AS4 __attribute__((address_space(4)))  // constant address space: scalar loads
 
 constexpr int NW = kWavesPerGroup;
+constexpr int NT_THREADS = NW * 64;
 
 template <typename T>
 struct Vec8;
@@ -90,6 +106,64 @@ __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// four consecutive outputs, rounded to nearest even
+template <typename T>
+__device__ __forceinline__ void store4(T* p, f32x4 v) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4*>(p) = v;
+  } else {
+    T t[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = (T)v[e];
+    *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, t);
+  }
+}
+
+// Partial results cross workgroups (and XCDs, whose L2 caches are not coherent with
+// each other) inside one launch.  They are written and read with device-scope
+// accesses, which go to the device's coherence point instead of a private L2, so no
+// cache-wide write-back or invalidate is needed: a writer waits for its stores to
+// complete (vmcnt 0) before a barrier and the arrival count; a reader that saw the
+// count complete reads with device-scope loads.
+__device__ __forceinline__ void st_dev(float* p, f32x4 v) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  __hip_atomic_store(q, (uint64_t)u[0] | ((uint64_t)u[1] << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, (uint64_t)u[2] | ((uint64_t)u[3] << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev2(float* p, float a, float b) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p),
+                     (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 ld_dev(const float* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(f32x4, u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b,
+                                         (uint32_t)(b >> 32)});
+}
+// (max, sum) pair of one partial
+__device__ __forceinline__ void ld_dev2(const float* p, float& a, float& b) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  a = __uint_as_float((uint32_t)v);
+  b = __uint_as_float((uint32_t)(v >> 32));
+}
+// every store this wave has issued is complete (and, device-scope, visible device-wide)
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
 
 // Registers of one 32-token chunk for one lane (column c = lane % 16, quad i = lane / 16).
 template <typename T, int D>
@@ -126,8 +200,64 @@ __device__ __forceinline__ f32x4 qk_tile(const u32x4 (&k)[Chunk<T, D>::KL],
   return acc;
 }
 
+// Log-sum-exp combination of cnt partials for each of nh heads.  Head hh's partials
+// are slots (row0 + hh) * stride + first + i, i < cnt, of (src_o, src_ml); the result
+// goes to the output rows (normalised, rounded) when out is given, else to slot
+// (row0 + hh) * dstride + dslot of (dst_o, dst_ml).  Partials are combined in slot
+// order, so the result is the same whoever runs it.
+template <typename T, int D>
+__device__ void merge_partials(const float* src_o, const float* src_ml, int64_t row0, int stride,
+                               int first, int cnt, int nh, T* out, float* dst_o, float* dst_ml,
+                               int dstride, int dslot) {
+  constexpr int C4 = D / 4;
+  for (int it = threadIdx.x; it < nh * C4; it += NT_THREADS) {
+    const int hh = it / C4, c = it - hh * C4;
+    const int64_t base = (row0 + hh) * stride + first;
+    const float* ml = src_ml + 2 * base;
+    const float* o = src_o + base * D + 4 * c;
+    // Loads go out in batches of 8 before any is used: device-scope loads keep
+    // program order, so a use right after each load would wait on each one.
+    float M = -INFINITY;
+    for (int i0 = 0; i0 < cnt; i0 += 8) {
+      float mv[8], lv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ld_dev2(ml + 2 * min(i0 + k, cnt - 1), mv[k], lv[k]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (i0 + k < cnt) M = fmaxf(M, mv[k]);
+    }
+    float Ls = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < cnt; i0 += 8) {
+      float mv[8], lv[8];
+      f32x4 ov[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = min(i0 + k, cnt - 1);
+        ld_dev2(ml + 2 * i, mv[k], lv[k]);
+        ov[k] = ld_dev(o + (int64_t)i * D);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (i0 + k < cnt) {
+          const float w = exp2_fast(mv[k] - M);
+          Ls += w * lv[k];
+          O += w * ov[k];
+        }
+      }
+    }
+    if (out) {
+      store4(out + (row0 + hh) * D + 4 * c, O / Ls);
+    } else {
+      const int64_t d = (row0 + hh) * dstride + dslot;
+      st_dev(dst_o + d * D + 4 * c, O);
+      if (c == 0) st_dev2(dst_ml + 2 * d, M, Ls);
+    }
+  }
+}
+
 template <typename T, int D, int BS>
-__global__ __launch_bounds__(NW * 64) void decode_partitions_kernel(DecodeParams P) {
+__global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_kernel(DecodeParams P) {
   typedef Chunk<T, D> C;
   constexpr int IDS = 32 / BS;  // physical blocks a 32-token chunk spans
   constexpr int NT = C::NT;
@@ -137,50 +267,119 @@ __global__ __launch_bounds__(NW * 64) void decode_partitions_kernel(DecodeParams
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
   __shared__ int sm_bad[NW];
+  __shared__ int sm_len[kScanMax];       // seq_lens of the launch's sequences
+  __shared__ int sm_full[kScanMax + 1];  // exclusive prefix count of full partitions
+  __shared__ int sm_class[kScanMax];     // size class of each sequence's last partition
+  __shared__ int sm_last[kScanMax];      // sequences in the order their last partitions run
+  __shared__ int sm_ccount[kScanMax / 64][kSizeClasses];
+  __shared__ int sm_ctotal[kSizeClasses];
+  __shared__ int sm_cbase[kSizeClasses];
+  __shared__ int sm_wsum[NW];
+  __shared__ int sm_next[2];  // by item parity: an item may pass no barrier before the next write
+  __shared__ int sm_flag[2];
 
-  const int p = blockIdx.x;
-  const int g = blockIdx.y / P.head_tiles;
-  const int ht = blockIdx.y - g * P.head_tiles;
-  const int s = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15;
   const int quad = lane >> 4;
-  const int Hq = P.num_q_heads;
-  const int hbase = g * P.group + ht * 16;    // first query head of this tile
-  const int nh = min(16, P.group - ht * 16);  // query heads in this tile
+  const int S = P.num_seqs, Hq = P.num_q_heads, PT = P.part_tokens;
+  const int HT2 = P.num_kv_heads * P.head_tiles;
 
-  const int L = ((const int32_t AS4*)P.seq_lens)[s];
-  if (L <= 0 || L > P.max_tokens) {
-    // empty sequence -> zeros; a length the table cannot hold -> NaN rows
-    if (p == 0) {
-      const T fill = (T)(L == 0 ? 0.f : __builtin_nanf(""));
-      T* o = (T*)P.out + ((int64_t)s * Hq + hbase) * D;
-      for (int i = threadIdx.x; i < nh * D; i += NW * 64) o[i] = fill;
-    }
-    return;
-  }
-  const int t_begin = p * P.part_tokens;
-  if (t_begin >= L) return;
-  const int t_end = min(L, t_begin + P.part_tokens);
-  const int nparts = (L + P.part_tokens - 1) / P.part_tokens;
-  const int nchunks = (t_end - t_begin + 31) >> 5;
-  const int last_blk = (L - 1) / BS;  // last table entry the sequence uses
-
-  // query fragment: lane (c, i) holds the same slice of q[head c] that it holds of
-  // each key row
-  const bool hvalid = col < nh;
-  const T* qrow = (const T*)P.q + ((int64_t)s * Hq + hbase + (hvalid ? col : 0)) * D + quad * EPL;
-  u32x4 qf[C::KL];
+  // ---------------------------------------------------------------- plan
+  // thread t looks at sequences 4t .. 4t+3: number of full partitions and the size
+  // class of the last one (class 0: an empty or invalid sequence, a one-item fill)
+  {
+    int nfull[4], sum = 0;
 #pragma unroll
-  for (int c = 0; c < C::KL; ++c)
-    qf[c] = hvalid ? ld16(qrow + c * 4 * EPL) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 4; ++i) {
+      const int s = 4 * tid + i;
+      nfull[i] = 0;
+      if (s < S) {
+        const int L = P.seq_lens[s];
+        sm_len[s] = L;
+        int cls = 0;
+        if (L > 0 && L <= P.max_tokens) {
+          const int n = (L + PT - 1) / PT;
+          const int r = L - (n - 1) * PT;  // tokens in the last partition, 1..PT
+          nfull[i] = n - 1;
+          cls = 1 + (int)min((int64_t)(kSizeClasses - 2),
+                             ((int64_t)(r - 1) * (kSizeClasses - 1)) / PT);
+        }
+        sm_class[s] = cls;
+      }
+      sum += nfull[i];
+    }
+    const int incl = wave_incl_scan(sum, lane);
+    if (lane == 63) sm_wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += sm_wsum[w];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = 4 * tid + i;
+      if (s < S) sm_full[s] = run;
+      run += nfull[i];
+    }
+    if (tid == 0) {
+      int F = 0;
+      for (int w = 0; w < NW; ++w) F += sm_wsum[w];
+      sm_full[S] = F;
+    }
+  }
+  __syncthreads();
+  // stable counting sort of the sequences by size class, largest class first
+  const int ngroups = (S + 63) / 64;
+  for (int j = wave; j < ngroups; j += NW) {
+    const int s = 64 * j + lane;
+    const int cls = s < S ? sm_class[s] : -1;
+    int c = 0;
+#pragma unroll
+    for (int b = 0; b < kSizeClasses; ++b) {
+      const int n = __popcll(__ballot(cls == b));
+      if (lane == b) c = n;
+    }
+    if (lane < kSizeClasses) sm_ccount[j][lane] = c;
+  }
+  __syncthreads();
+  if (tid < kSizeClasses) {
+    int run = 0;
+    for (int j = 0; j < ngroups; ++j) {
+      const int c = sm_ccount[j][tid];
+      sm_ccount[j][tid] = run;  // sequences of this class in earlier groups
+      run += c;
+    }
+    sm_ctotal[tid] = run;
+  }
+  __syncthreads();
+  if (tid < kSizeClasses) {
+    int base = 0;
+    for (int b = tid + 1; b < kSizeClasses; ++b) base += sm_ctotal[b];
+    sm_cbase[tid] = base;
+  }
+  __syncthreads();
+  for (int j = wave; j < ngroups; j += NW) {
+    const int s = 64 * j + lane;
+    const int cls = s < S ? sm_class[s] : -1;
+    uint64_t same = 0;
+#pragma unroll
+    for (int b = 0; b < kSizeClasses; ++b) {
+      const uint64_t m = __ballot(cls == b);
+      if (cls == b) same = m;
+    }
+    if (s < S) {
+      const int rank = __popcll(same & ((1ull << lane) - 1ull));
+      sm_last[sm_cbase[cls] + sm_ccount[j][cls] + rank] = s;
+    }
+  }
+  __syncthreads();
+  const int F = sm_full[S];
+  const int total = (F + S) * HT2;  // the host keeps this below 2^31
 
+  // table entries are int32, so a pool larger than INT32_MAX blocks accepts them all
+  const uint32_t nblk32 = (uint32_t)min(P.num_blocks, (int64_t)0x7fffffff);
   const int64_t tile = (int64_t)BS * D;  // elements of one (block, KV head) tile
   const int64_t blk_stride = (int64_t)P.num_kv_heads * tile;
-  const T* kbase = (const T*)P.k_cache + (int64_t)g * tile;
-  const T* vbase = (const T*)P.v_cache + (int64_t)g * tile;
-  const int32_t AS4* tbl = (const int32_t AS4*)(P.block_tables + (int64_t)s * P.max_blocks);
 
   // lane-constant positions inside a chunk
   const int ka = 8 * (col >> 2) + (col & 3);  // token of this lane's key row, tile a
@@ -190,353 +389,382 @@ __global__ __launch_bounds__(NW * 64) void decode_partitions_kernel(DecodeParams
   const int rv = (8 * quad) / BS;  // block of this lane's 8 value tokens (BS >= 8)
   const int vofs = (BS >= 8) ? col * BS + (8 * quad) % BS : col * BS;
 
-  // table entries are int32, so a pool larger than INT32_MAX blocks accepts them all
-  const uint32_t nblk32 = (uint32_t)min(P.num_blocks, (int64_t)0x7fffffff);
+  // ---------------------------------------------------------------- items
+  int item = blockIdx.x;
+  for (int iter = 0; item < total; ++iter) {
+    int next = 0;
+    if (tid == 0) next = (int)gridDim.x + atomicAdd(P.queue, 1);
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int bad = 0;
-
-  auto issue = [&](C& c, int t0) {
-    int ids[IDS];
-    const int j0 = t0 / BS;
-    // entries past the sequence's last block are never read; their tokens are
-    // masked, so the last block stands in for them
-#pragma unroll
-    for (int i = 0; i < IDS; ++i) ids[i] = tbl[min(j0 + i, last_blk)];
-#pragma unroll
-    for (int i = 0; i < IDS; ++i) {
-      const bool ok = (uint32_t)ids[i] < nblk32;
-      bad |= !ok;
-      ids[i] = ok ? ids[i] : 0;
-    }
-    // per-lane choice among the chunk's (uniform) block ids
-    int idlanes = 0;
-    if constexpr (IDS > 2) {
-#pragma unroll
-      for (int i = 0; i < IDS; ++i) {
-        const int sid = __builtin_amdgcn_readfirstlane(ids[i]);
-        asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(idlanes) : "s"(sid), "i"(i));
+    const int j = item / HT2;
+    const int gt = item - j * HT2;
+    const int g = gt / P.head_tiles;
+    const int ht = gt - g * P.head_tiles;
+    int s, p;
+    if (j < F) {  // a full partition: find s with sm_full[s] <= j < sm_full[s + 1]
+      int lo = 0, hi = S;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sm_full[mid] <= j) lo = mid;
+        else hi = mid;
       }
+      s = lo;
+      p = j - sm_full[s];
+    } else {  // a sequence's last partition
+      s = sm_last[j - F];
+      p = -1;
     }
-    auto pick = [&](int r) {
-      if constexpr (IDS == 1) return ids[0];
-      else if constexpr (IDS == 2) return r ? ids[1] : ids[0];
-      else return __builtin_amdgcn_ds_bpermute(r << 2, idlanes);
-    };
-    const T* pa = kbase + (int64_t)pick(ra) * blk_stride + kofs_a;
-    const T* pb = kbase + (int64_t)pick(rb) * blk_stride + kofs_b;
+    s = __builtin_amdgcn_readfirstlane(s);
+    p = __builtin_amdgcn_readfirstlane(p);
+    const int L = __builtin_amdgcn_readfirstlane(sm_len[s]);
+    const int hbase = g * P.group + ht * 16;    // first query head of this tile
+    const int nh = min(16, P.group - ht * 16);  // query heads in this tile
+    const int64_t row0 = (int64_t)s * Hq + hbase;
+
+    if (L <= 0 || L > P.max_tokens) {
+      // empty sequence -> zeros; a length the table cannot hold -> NaN rows
+      const float fill = L == 0 ? 0.f : __builtin_nanf("");
+      T* o = (T*)P.out + row0 * D;
+      for (int i = tid; i < nh * D; i += NT_THREADS) o[i] = (T)fill;
+    } else {
+      const int n = (L + PT - 1) / PT;
+      if (p < 0) p = n - 1;
+      const int t_begin = p * PT;
+      const int t_end = min(L, t_begin + PT);
+      const int nchunks = (t_end - t_begin + 31) >> 5;
+      const int last_blk = (L - 1) / BS;  // last table entry the sequence uses
+
+      // query fragment: lane (c, i) holds the same slice of q[head c] that it holds
+      // of each key row
+      const bool hvalid = col < nh;
+      const T* qrow = (const T*)P.q + (row0 + (hvalid ? col : 0)) * D + quad * EPL;
+      u32x4 qf[C::KL];
 #pragma unroll
-    for (int k = 0; k < C::KL; ++k) {
-      c.ka[k] = ld16(pa + k * 4 * EPL);
-      c.kb[k] = ld16(pb + k * 4 * EPL);
-    }
-    if constexpr (BS >= 8) {
-      const T* pv = vbase + (int64_t)pick(rv) * blk_stride + vofs;
+      for (int c = 0; c < C::KL; ++c)
+        qf[c] = hvalid ? ld16(qrow + c * 4 * EPL) : u32x4{0u, 0u, 0u, 0u};
+
+      const T* kbase = (const T*)P.k_cache + (int64_t)g * tile;
+      const T* vbase = (const T*)P.v_cache + (int64_t)g * tile;
+      const int32_t AS4* tbl = (const int32_t AS4*)(P.block_tables + (int64_t)s * P.max_blocks);
+
+      float m_run = -INFINITY, l_run = 0.f;
+      f32x4 acc[NT];
 #pragma unroll
-      for (int n = 0; n < NT; ++n)
+      for (int nn = 0; nn < NT; ++nn) acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+      int bad = 0;
+
+      auto issue = [&](C& c, int t0) {
+        int ids[IDS];
+        const int j0 = t0 / BS;
+        // entries past the sequence's last block are never read; their tokens are
+        // masked, so the last block stands in for them
 #pragma unroll
-        for (int u = 0; u < C::VL; ++u) c.v[n][u] = ld16(pv + n * 16 * BS + u * EPL);
-    } else {  // BS == 4: the 8 tokens straddle two blocks
-      const T* lo = vbase + (int64_t)pick(2 * quad) * blk_stride + vofs;
-      const T* hi = vbase + (int64_t)pick(2 * quad + 1) * blk_stride + vofs;
+        for (int i = 0; i < IDS; ++i) ids[i] = tbl[min(j0 + i, last_blk)];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        if constexpr (sizeof(T) == 2) {
-          const u32x2 a = ld8(lo + n * 16 * BS), b = ld8(hi + n * 16 * BS);
-          c.v[n][0] = u32x4{a[0], a[1], b[0], b[1]};
-        } else {
-          c.v[n][0] = ld16(lo + n * 16 * BS);
-          c.v[n][1] = ld16(hi + n * 16 * BS);
+        for (int i = 0; i < IDS; ++i) {
+          const bool ok = (uint32_t)ids[i] < nblk32;
+          bad |= !ok;
+          ids[i] = ok ? ids[i] : 0;
         }
-      }
-    }
-  };
+        // per-lane choice among the chunk's (uniform) block ids
+        int idlanes = 0;
+        if constexpr (IDS > 2) {
+#pragma unroll
+          for (int i = 0; i < IDS; ++i) {
+            const int sid = __builtin_amdgcn_readfirstlane(ids[i]);
+            asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(idlanes) : "s"(sid), "i"(i));
+          }
+        }
+        auto pick = [&](int r) {
+          if constexpr (IDS == 1) return ids[0];
+          else if constexpr (IDS == 2) return r ? ids[1] : ids[0];
+          else return __builtin_amdgcn_ds_bpermute(r << 2, idlanes);
+        };
+        const T* pa = kbase + (int64_t)pick(ra) * blk_stride + kofs_a;
+        const T* pb = kbase + (int64_t)pick(rb) * blk_stride + kofs_b;
+#pragma unroll
+        for (int k = 0; k < C::KL; ++k) {
+          c.ka[k] = ld16(pa + k * 4 * EPL);
+          c.kb[k] = ld16(pb + k * 4 * EPL);
+        }
+        if constexpr (BS >= 8) {
+          const T* pv = vbase + (int64_t)pick(rv) * blk_stride + vofs;
+#pragma unroll
+          for (int nn = 0; nn < NT; ++nn)
+#pragma unroll
+            for (int u = 0; u < C::VL; ++u) c.v[nn][u] = ld16(pv + nn * 16 * BS + u * EPL);
+        } else {  // BS == 4: the 8 tokens straddle two blocks
+          const T* lo = vbase + (int64_t)pick(2 * quad) * blk_stride + vofs;
+          const T* hi = vbase + (int64_t)pick(2 * quad + 1) * blk_stride + vofs;
+#pragma unroll
+          for (int nn = 0; nn < NT; ++nn) {
+            if constexpr (sizeof(T) == 2) {
+              const u32x2 a = ld8(lo + nn * 16 * BS), b = ld8(hi + nn * 16 * BS);
+              c.v[nn][0] = u32x4{a[0], a[1], b[0], b[1]};
+            } else {
+              c.v[nn][0] = ld16(lo + nn * 16 * BS);
+              c.v[nn][1] = ld16(hi + nn * 16 * BS);
+            }
+          }
+        }
+      };
 
-  auto compute = [&](C& c, int t0) {
-    const f32x4 sa = qk_tile<T, D>(c.ka, qf);
-    const f32x4 sb = qk_tile<T, D>(c.kb, qf);
-    float z[8];
+      auto compute = [&](C& c, int t0) {
+        const f32x4 sa = qk_tile<T, D>(c.ka, qf);
+        const f32x4 sb = qk_tile<T, D>(c.kb, qf);
+        float z[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      z[e] = sa[e] * P.scale_log2;      // token t0 + 8i + e
-      z[4 + e] = sb[e] * P.scale_log2;  // token t0 + 8i + 4 + e
-    }
-    const int tfirst = t0 + 8 * quad;
-    const bool tail = t0 + 32 > t_end;  // uniform: only the last chunk of a partition
-    if (tail) {
+        for (int e = 0; e < 4; ++e) {
+          z[e] = sa[e] * P.scale_log2;      // token t0 + 8i + e
+          z[4 + e] = sb[e] * P.scale_log2;  // token t0 + 8i + 4 + e
+        }
+        const int tfirst = t0 + 8 * quad;
+        const bool tail = t0 + 32 > t_end;  // uniform: only the last chunk of an item
+        if (tail) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) z[e] = (tfirst + e < t_end) ? z[e] : -INFINITY;
-    }
-    float cm = z[0];
+          for (int e = 0; e < 8; ++e) z[e] = (tfirst + e < t_end) ? z[e] : -INFINITY;
+        }
+        float cm = z[0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, z[e]);
-    cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
-    const float m_new = fmaxf(m_run, cm);
-    const float alpha = exp2_fast(m_run - m_new);
-    float pr[8], psum = 0.f;
+        for (int e = 1; e < 8; ++e) cm = fmaxf(cm, z[e]);
+        cm = fmaxf(cm, __shfl_xor(cm, 16));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        const float m_new = fmaxf(m_run, cm);
+        const float alpha = exp2_fast(m_run - m_new);
+        float pr[8], psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pr[e] = exp2_fast(z[e] - m_new);
-      psum += pr[e];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+        for (int e = 0; e < 8; ++e) {
+          pr[e] = exp2_fast(z[e] - m_new);
+          psum += pr[e];
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+        for (int nn = 0; nn < NT; ++nn) acc[nn] *= alpha;
 
-    if (tail) {  // values past the end may be NaN: zero them, never multiply them
+        if (tail) {  // values past the end may be NaN: zero them, never multiply them
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
+          for (int nn = 0; nn < NT; ++nn) {
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                const uint32_t keep = ((tfirst + 2 * w < t_end) ? 0x0000FFFFu : 0u) |
+                                      ((tfirst + 2 * w + 1 < t_end) ? 0xFFFF0000u : 0u);
+                c.v[nn][0][w] &= keep;
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                c.v[nn][e >> 2][e & 3] = (tfirst + e < t_end) ? c.v[nn][e >> 2][e & 3] : 0u;
+            }
+          }
+        }
         if constexpr (sizeof(T) == 2) {
+          // weights as hi + lo pairs of the input type: the sum of two products keeps
+          // ~16 significant bits of each fp32 weight, so the weighted sum is as exact
+          // as an fp32 one and the only rounding left is the final store
+          typedef typename Vec8<T>::type V8;
+          V8 phi, plo;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t keep = ((tfirst + 2 * w < t_end) ? 0x0000FFFFu : 0u) |
-                                  ((tfirst + 2 * w + 1 < t_end) ? 0xFFFF0000u : 0u);
-            c.v[n][0][w] &= keep;
+          for (int e = 0; e < 8; ++e) {
+            const T h = (T)pr[e];
+            phi[e] = h;
+            plo[e] = (T)(pr[e] - (float)h);
+          }
+#pragma unroll
+          for (int nn = 0; nn < NT; ++nn) {
+            const V8 vv = __builtin_bit_cast(V8, c.v[nn][0]);
+            acc[nn] = mma16(vv, phi, acc[nn]);
+            acc[nn] = mma16(vv, plo, acc[nn]);
           }
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            c.v[n][e >> 2][e & 3] = (tfirst + e < t_end) ? c.v[n][e >> 2][e & 3] : 0u;
+          for (int nn = 0; nn < NT; ++nn) {
+            const f32x4 lo = __builtin_bit_cast(f32x4, c.v[nn][0]);
+            const f32x4 hi = __builtin_bit_cast(f32x4, c.v[nn][1]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[nn] = mma4(lo[e], pr[e], acc[nn]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[nn] = mma4(hi[e], pr[4 + e], acc[nn]);
+          }
+        }
+      };
+
+      // this wave's chunks are wave, wave + NW, ...; two buffers alternate so the
+      // next chunk's loads are in flight while this one is computed
+      const int nc = wave < nchunks ? (nchunks - wave + NW - 1) / NW : 0;
+      auto t_of = [&](int i) { return t_begin + 32 * (wave + NW * i); };
+      if (nc > 0) {
+        C A, B;
+        issue(A, t_of(0));
+        int i = 0;
+        for (; i + 2 < nc; i += 2) {
+          issue(B, t_of(i + 1));
+          compute(A, t_of(i));
+          issue(A, t_of(i + 2));
+          compute(B, t_of(i + 1));
+        }
+        if (i + 1 < nc) {
+          issue(B, t_of(i + 1));
+          compute(A, t_of(i));
+          compute(B, t_of(i + 1));
+        } else {
+          compute(A, t_of(i));
+        }
+      }
+
+      // merge the four waves (fixed order) through LDS
+      l_run += __shfl_xor(l_run, 16);
+      l_run += __shfl_xor(l_run, 32);
+      if (quad == 0) {
+        sm_m[wave][col] = m_run;
+        sm_l[wave][col] = l_run;
+      }
+#pragma unroll
+      for (int nn = 0; nn < NT; ++nn)
+        *reinterpret_cast<f32x4*>(&sm_o[wave][col][16 * nn + 4 * quad]) = acc[nn];
+      if (lane == 0) sm_bad[wave] = bad;
+      __syncthreads();
+
+      int anybad = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) anybad |= sm_bad[w];
+      for (int it = tid; it < nh * (D / 4); it += NT_THREADS) {
+        const int hh = it / (D / 4);
+        const int d4 = (it - hh * (D / 4)) * 4;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][hh]);
+        float Ls = 0.f;
+        f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float mw = sm_m[w][hh];
+          if (mw == -INFINITY) continue;  // this wave had no chunk
+          const float e = exp2_fast(mw - M);
+          Ls += e * sm_l[w][hh];
+          O += e * *reinterpret_cast<const f32x4*>(&sm_o[w][hh][d4]);
+        }
+        if (anybad) {
+          const float nan = __builtin_nanf("");
+          M = Ls = nan;
+          O = f32x4{nan, nan, nan, nan};
+        }
+        if (n == 1) {
+          store4((T*)P.out + (row0 + hh) * D + d4, O / Ls);
+        } else {
+          const int64_t slot = (row0 + hh) * P.pmax + p;
+          st_dev(P.part_o + slot * D + d4, O);
+          if (d4 == 0) st_dev2(P.part_ml + 2 * slot, M, Ls);
+        }
+      }
+
+      if (n > 1) {
+        // publish this partition, then count it in its group of kMergeFan
+        stores_done();
+        __syncthreads();
+        const int grp = p / kMergeFan;
+        const int gsize = min(kMergeFan, n - grp * kMergeFan);
+        const int ngrp = (n + kMergeFan - 1) / kMergeFan;
+        if (tid == 0) {
+          int* cnt = P.node_count + ((int64_t)s * HT2 + gt) * P.nodes + grp;
+          const int before = atomicAdd(cnt, 1);
+          const int done = before == gsize - 1;
+          if (done) atomicExch(cnt, 0);  // every member has arrived: ready for the next call
+          sm_flag[0] = done;
+        }
+        __syncthreads();
+        if (sm_flag[0]) {
+          if (ngrp == 1) {
+            merge_partials<T, D>(P.part_o, P.part_ml, row0, P.pmax, 0, n, nh, (T*)P.out,
+                                 nullptr, nullptr, 0, 0);
+          } else {
+            merge_partials<T, D>(P.part_o, P.part_ml, row0, P.pmax, grp * kMergeFan, gsize, nh,
+                                 (T*)nullptr, P.node_o, P.node_ml, P.nodes, grp);
+            stores_done();
+            __syncthreads();
+            if (tid == 0) {
+              int* cnt = P.root_count + (int64_t)s * HT2 + gt;
+              const int before = atomicAdd(cnt, 1);
+              const int done = before == ngrp - 1;
+              if (done) atomicExch(cnt, 0);
+              sm_flag[1] = done;
+            }
+            __syncthreads();
+            if (sm_flag[1]) {
+              merge_partials<T, D>(P.node_o, P.node_ml, row0, P.nodes, 0, ngrp, nh, (T*)P.out,
+                                   nullptr, nullptr, 0, 0);
+            }
+          }
         }
       }
     }
-    if constexpr (sizeof(T) == 2) {
-      // weights as hi + lo pairs of the input type: the sum of two products keeps
-      // ~16 significant bits of each fp32 weight, so the weighted sum is as exact as
-      // an fp32 one and the only rounding left is the final store
-      typedef typename Vec8<T>::type V8;
-      V8 phi, plo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const T h = (T)pr[e];
-        phi[e] = h;
-        plo[e] = (T)(pr[e] - (float)h);
-      }
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const V8 vv = __builtin_bit_cast(V8, c.v[n][0]);
-        acc[n] = mma16(vv, phi, acc[n]);
-        acc[n] = mma16(vv, plo, acc[n]);
-      }
-    } else {
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const f32x4 lo = __builtin_bit_cast(f32x4, c.v[n][0]);
-        const f32x4 hi = __builtin_bit_cast(f32x4, c.v[n][1]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[n] = mma4(lo[e], pr[e], acc[n]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[n] = mma4(hi[e], pr[4 + e], acc[n]);
-      }
-    }
-  };
 
-  // Software pipeline: the next chunk's 16 loads are issued before this chunk's
-  // math, so they are in flight while it runs (the compiler's wait counts keep
-  // them outstanding; the buffer copy at the end of an iteration is register
-  // renaming the compiler turns into moves).
-  int ck = wave;
-  if (ck < nchunks) {
-    C A;
-    issue(A, t_begin + 32 * ck);
-    while (ck + NW < nchunks) {
-      C B;
-      issue(B, t_begin + 32 * (ck + NW));
-      compute(A, t_begin + 32 * ck);
-      A = B;
-      ck += NW;
-    }
-    compute(A, t_begin + 32 * ck);
+    // Two slots: thread 0 may write the next item's slot before a slow wave has read
+    // this one only if the item in between passes no barrier (the fill path).
+    if (tid == 0) sm_next[iter & 1] = next;
+    __syncthreads();  // also: every thread is done with this item's LDS
+    item = sm_next[iter & 1];
   }
 
-  // merge the four waves (fixed order) through LDS
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (quad == 0) {
-    sm_m[wave][col] = m_run;
-    sm_l[wave][col] = l_run;
-  }
-#pragma unroll
-  for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(&sm_o[wave][col][16 * n + 4 * quad]) = acc[n];
-  if (lane == 0) sm_bad[wave] = bad;
-  __syncthreads();
-
-  int anybad = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) anybad |= sm_bad[w];
-  for (int it = threadIdx.x; it < nh * (D / 4); it += NW * 64) {
-    const int hh = it / (D / 4);
-    const int d4 = (it - hh * (D / 4)) * 4;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][hh]);
-    float Ls = 0.f;
-    f32x4 O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = sm_m[w][hh];
-      if (mw == -INFINITY) continue;  // this wave had no chunk
-      const float e = exp2_fast(mw - M);
-      Ls += e * sm_l[w][hh];
-      O += e * *reinterpret_cast<const f32x4*>(&sm_o[w][hh][d4]);
+  // the last workgroup out resets the queue for the next call
+  if (tid == 0) {
+    const int before = atomicAdd(P.queue + 1, 1);
+    if (before == (int)gridDim.x - 1) {
+      atomicExch(P.queue, 0);
+      atomicExch(P.queue + 1, 0);
     }
-    if (anybad) {
-      const float nan = __builtin_nanf("");
-      M = Ls = nan;
-      O = f32x4{nan, nan, nan, nan};
-    }
-    const int64_t row = (int64_t)s * Hq + hbase + hh;
-    if (nparts == 1) {
-      T* o = (T*)P.out + row * D + d4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (T)(O[e] / Ls);
-    } else {
-      const int64_t slot = row * P.pmax + p;
-      *reinterpret_cast<f32x4*>(P.ws_o + slot * D + d4) = O;
-      if (d4 == 0) {
-        P.ws_ml[2 * slot] = M;
-        P.ws_ml[2 * slot + 1] = Ls;
-      }
-    }
-  }
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-// Log-sum-exp merge of a sequence's partitions, one workgroup per (query head,
-// sequence).  Fixed reduction order, so the result does not depend on timing.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams P) {
-  extern __shared__ float sm_w[];  // one weight per partition
-  __shared__ float sm_red[4];
-  __shared__ f32x4 sm_acc[256];
-  const int h = blockIdx.x, s = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int L = ((const int32_t AS4*)P.seq_lens)[s];
-  if (L <= P.part_tokens || L > P.max_tokens) return;  // finished by its single partition
-  const int nparts = (L + P.part_tokens - 1) / P.part_tokens;
-  const int64_t row = (int64_t)s * P.num_q_heads + h;
-  const float* ml = P.ws_ml + row * P.pmax * 2;
-  const float* o = P.ws_o + row * P.pmax * D;
-
-  float M = -INFINITY;
-  for (int q = tid; q < nparts; q += 256) M = fmaxf(M, ml[2 * q]);
-  M = wave_max(M);
-  if (lane == 0) sm_red[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(sm_red[0], sm_red[1]), fmaxf(sm_red[2], sm_red[3]));
-  __syncthreads();
-
-  float Ls = 0.f;
-  for (int q = tid; q < nparts; q += 256) {
-    const float w = exp2_fast(ml[2 * q] - M);
-    sm_w[q] = w;
-    Ls += w * ml[2 * q + 1];
-  }
-  Ls = wave_sum(Ls);
-  if (lane == 0) sm_red[wave] = Ls;
-  __syncthreads();
-  Ls = (sm_red[0] + sm_red[1]) + (sm_red[2] + sm_red[3]);
-
-  constexpr int C4 = D / 4;   // float4 columns of a row
-  constexpr int R = 256 / C4; // rows summed in parallel
-  const int r = tid / C4, c = tid - r * C4;
-  f32x4 a = {0.f, 0.f, 0.f, 0.f};
-  for (int q = r; q < nparts; q += R)
-    a += sm_w[q] * *reinterpret_cast<const f32x4*>(o + (int64_t)q * D + 4 * c);
-  sm_acc[tid] = a;
-  __syncthreads();
-  if (tid < C4) {
-    f32x4 t = sm_acc[tid];
-#pragma unroll
-    for (int rr = 1; rr < R; ++rr) t += sm_acc[rr * C4 + tid];
-    T* out = (T*)P.out + row * D + 4 * tid;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = (T)(t[e] / Ls);
   }
 }
 
 template <typename T, int D, int BS>
-hipError_t launch_parts(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.pmax, p.num_kv_heads * p.head_tiles, p.num_seqs);
-  DecodeParams arg = p;
-  void* args[] = {&arg};
-  return hipLaunchKernel((const void*)decode_partitions_kernel<T, D, BS>, grid, dim3(NW * 64),
-                         args, 0, stream);
+const void* kernel_of() {
+  return (const void*)decode_kernel<T, D, BS>;
 }
 
 template <typename T, int D>
-hipError_t launch_parts_bs(int bs, const DecodeParams& p, hipStream_t stream) {
+const void* kernel_bs(int bs) {
   switch (bs) {
-    case 4: return launch_parts<T, D, 4>(p, stream);
-    case 8: return launch_parts<T, D, 8>(p, stream);
-    case 16: return launch_parts<T, D, 16>(p, stream);
-    case 32: return launch_parts<T, D, 32>(p, stream);
+    case 4: return kernel_of<T, D, 4>();
+    case 8: return kernel_of<T, D, 8>();
+    case 16: return kernel_of<T, D, 16>();
+    case 32: return kernel_of<T, D, 32>();
   }
-  return hipErrorInvalidValue;
+  return nullptr;
 }
 
 template <typename T>
-hipError_t launch_parts_d(int d, int bs, const DecodeParams& p, hipStream_t stream) {
+const void* kernel_d(int d, int bs) {
   switch (d) {
-    case 64: return launch_parts_bs<T, 64>(bs, p, stream);
-    case 128: return launch_parts_bs<T, 128>(bs, p, stream);
+    case 64: return kernel_bs<T, 64>(bs);
+    case 128: return kernel_bs<T, 128>(bs);
   }
-  return hipErrorInvalidValue;
+  return nullptr;
 }
 
-template <typename T, int D>
-hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.num_q_heads, p.num_seqs);
-  DecodeParams arg = p;
-  void* args[] = {&arg};
-  return hipLaunchKernel((const void*)decode_merge_kernel<T, D>, grid, dim3(256), args,
-                         sizeof(float) * (size_t)p.pmax, stream);
-}
-
-template <typename T>
-hipError_t launch_merge_d(int d, const DecodeParams& p, hipStream_t stream) {
-  switch (d) {
-    case 64: return launch_merge<T, 64>(p, stream);
-    case 128: return launch_merge<T, 128>(p, stream);
+const void* decode_kernel_for(int dtype, int head_dim, int block_size) {
+  switch (dtype) {
+    case 0: return kernel_d<float>(head_dim, block_size);
+    case 1: return kernel_d<_Float16>(head_dim, block_size);
+    case 2: return kernel_d<__bf16>(head_dim, block_size);
   }
-  return hipErrorInvalidValue;
+  return nullptr;
 }
 
 }  // namespace
 
-hipError_t launch_decode_partitions(int dtype, int head_dim, int block_size,
-                                    const DecodeParams& p, hipStream_t stream) {
-  switch (dtype) {
-    case 0: return launch_parts_d<float>(head_dim, block_size, p, stream);
-    case 1: return launch_parts_d<_Float16>(head_dim, block_size, p, stream);
-    case 2: return launch_parts_d<__bf16>(head_dim, block_size, p, stream);
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodeParams& p,
+                         int grid, hipStream_t stream) {
+  const void* k = decode_kernel_for(dtype, head_dim, block_size);
+  if (!k || grid <= 0) return hipErrorInvalidValue;
+  DecodeParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(k, dim3(grid), dim3(NT_THREADS), args, 0, stream);
 }
 
-hipError_t launch_decode_merge(int dtype, int head_dim, const DecodeParams& p,
-                               hipStream_t stream) {
-  switch (dtype) {
-    case 0: return launch_merge_d<float>(head_dim, p, stream);
-    case 1: return launch_merge_d<_Float16>(head_dim, p, stream);
-    case 2: return launch_merge_d<__bf16>(head_dim, p, stream);
-  }
-  return hipErrorInvalidValue;
+hipError_t decode_blocks_per_cu(int dtype, int head_dim, int block_size, int* blocks) {
+  const void* k = decode_kernel_for(dtype, head_dim, block_size);
+  if (!k) return hipErrorInvalidValue;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k, NT_THREADS, 0);
 }
 
 }  // namespace pa

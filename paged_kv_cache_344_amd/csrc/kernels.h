@@ -6,7 +6,16 @@
 
 namespace pa {
 
-// Everything a decode launch needs; passed by value as the kernel argument.
+constexpr int kWavesPerGroup = 4;   // waves sharing one work item
+constexpr int kScanMax = 1024;      // sequences one decode launch plans for (host slices above)
+constexpr int kMergeFan = 16;       // partials combined per merge node
+constexpr int kMaxPartitions = 8192;
+constexpr int kSizeClasses = 16;    // size classes the last partitions are ordered by
+
+// Everything a decode launch needs; passed by value as the kernel argument.  The
+// launch covers num_seqs sequences starting at the pointers given (the host slices
+// larger batches); counters and partial buffers are indexed by the slice's own
+// sequence numbers.
 struct DecodeParams {
   const void* q;                // [S][Hq][D]
   const void* k_cache;          // [N][Hkv][bs][D]
@@ -14,10 +23,15 @@ struct DecodeParams {
   const int32_t* block_tables;  // [S][max_blocks]
   const int32_t* seq_lens;      // [S]
   void* out;                    // [S][Hq][D]
-  float* ws_o;                  // [S][Hq][pmax][D]  unnormalised partition outputs
-  float* ws_ml;                 // [S][Hq][pmax][2]  (running max in log2 units, sum)
+  float* part_o;                // [S][Hq][pmax][D]   per-partition unnormalised outputs
+  float* part_ml;               // [S][Hq][pmax][2]   (running max in log2 units, sum)
+  float* node_o;                // [S][Hq][nodes][D]  merged groups of kMergeFan partitions
+  float* node_ml;               // [S][Hq][nodes][2]
+  int32_t* queue;               // [2]: next work item, finished workgroups (0 between calls)
+  int32_t* node_count;          // [S][Hkv*tiles][nodes]: partitions finished per group
+  int32_t* root_count;          // [S][Hkv*tiles]: groups finished per sequence and head tile
   int64_t num_blocks;           // N
-  int32_t num_seqs;             // S
+  int32_t num_seqs;             // S of this launch (<= kScanMax)
   int32_t num_q_heads;          // Hq
   int32_t num_kv_heads;         // Hkv
   int32_t group;                // Hq / Hkv
@@ -26,6 +40,7 @@ struct DecodeParams {
   int32_t max_tokens;           // max_blocks * bs
   int32_t part_tokens;          // tokens per partition, a multiple of 32
   int32_t pmax;                 // ceil(max_tokens / part_tokens)
+  int32_t nodes;                // ceil(pmax / kMergeFan)
   float scale_log2;             // scale * log2(e): logits are kept in base-2 units
 };
 
@@ -45,13 +60,10 @@ struct CacheWriteParams {
 // dtype codes follow pa_dtype: 0 f32, 1 f16, 2 bf16.
 // Each returns hipErrorInvalidValue for a (dtype, head_dim, block_size) that has
 // no compiled instance; the caller checks support first.
-hipError_t launch_decode_partitions(int dtype, int head_dim, int block_size,
-                                    const DecodeParams& p, hipStream_t stream);
-hipError_t launch_decode_merge(int dtype, int head_dim, const DecodeParams& p,
-                               hipStream_t stream);
+hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodeParams& p,
+                         int grid, hipStream_t stream);
+// Workgroups of the decode kernel that fit on one compute unit at once.
+hipError_t decode_blocks_per_cu(int dtype, int head_dim, int block_size, int* blocks);
 hipError_t launch_cache_write(int elem_bytes, const CacheWriteParams& p, hipStream_t stream);
-
-constexpr int kMaxPartitions = 8192;  // merge kernel keeps one weight per partition in LDS
-constexpr int kWavesPerGroup = 4;     // waves sharing one (sequence, KV head, partition)
 
 }  // namespace pa

@@ -2,11 +2,14 @@
 //
 // Every host-side argument is checked before the first HIP call, so a bad call
 // returns a status without touching the GPU (and can be tested on a machine with
-// none).  The library owns no device memory: the split-K workspace is the
-// caller's, sized by pa_decode_workspace_bytes.
+// none).  The library owns no device memory: the decode workspace (work queue,
+// merge counters, split-K partials) is the caller's, sized by
+// pa_decode_workspace_bytes.
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <string>
 
@@ -38,12 +41,15 @@ constexpr int kDefaultPartition = 512;
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Where everything lives inside a decode workspace (byte offsets).
 struct Plan {
   int32_t part_tokens;
-  int32_t pmax;
+  int32_t pmax;        // partitions a sequence can have
+  int32_t nodes;       // groups of kMergeFan partitions
   int32_t head_tiles;
   int32_t max_tokens;
-  size_t ws_o_bytes;  // 0 when no split is possible
+  int32_t slice;       // sequences per launch
+  size_t off_node_count, off_root_count, off_part_o, off_part_ml, off_node_o, off_node_ml;
   size_t ws_bytes;
 };
 
@@ -79,18 +85,60 @@ pa_status plan_decode(const pa_decode_ext* ext, int32_t bs, int32_t hkv, Plan* p
                 (long long)pmax, pa::kMaxPartitions);
   const int32_t G = Hq / hkv;
   const int32_t tiles = (G + 15) / 16;
-  if ((int64_t)hkv * tiles > 65535) return fail(PA_ERR_UNSUPPORTED, "too many KV heads for one launch");
+  const int64_t ht2 = (int64_t)hkv * tiles;
+  if (ht2 > 65535) return fail(PA_ERR_UNSUPPORTED, "too many KV heads for one launch");
+  const int64_t nodes = (pmax + pa::kMergeFan - 1) / pa::kMergeFan;
+  // work items of one launch, (full + last partitions) x head tiles, stay below 2^31
+  const int64_t slice = std::min<int64_t>(pa::kScanMax, (INT32_MAX - (1 << 20)) / (pmax * ht2));
   pl->part_tokens = (int32_t)part;
   pl->pmax = (int32_t)pmax;
+  pl->nodes = (int32_t)nodes;
   pl->head_tiles = tiles;
   pl->max_tokens = (int32_t)max_tokens;
-  if (pmax > 1) {
-    const size_t rows = (size_t)S * Hq * (size_t)pmax;
-    pl->ws_o_bytes = round_up(rows * D * sizeof(float), kAlign);
-    pl->ws_bytes = pl->ws_o_bytes + round_up(rows * 2 * sizeof(float), kAlign);
-  } else {
-    pl->ws_o_bytes = pl->ws_bytes = 0;
+  pl->slice = (int32_t)slice;
+  // [queue: 2 ints][node counts][root counts][partition partials][group partials]
+  size_t off = kAlign;
+  pl->off_node_count = off;
+  off = round_up(off + (size_t)S * ht2 * nodes * sizeof(int32_t), kAlign);
+  pl->off_root_count = off;
+  off = round_up(off + (size_t)S * ht2 * sizeof(int32_t), kAlign);
+  const size_t rows = (size_t)S * Hq;
+  pl->off_part_o = off;
+  if (pmax > 1) off = round_up(off + rows * pmax * D * sizeof(float), kAlign);
+  pl->off_part_ml = off;
+  if (pmax > 1) off = round_up(off + rows * pmax * 2 * sizeof(float), kAlign);
+  pl->off_node_o = off;
+  if (nodes > 1) off = round_up(off + rows * nodes * D * sizeof(float), kAlign);
+  pl->off_node_ml = off;
+  if (nodes > 1) off = round_up(off + rows * nodes * 2 * sizeof(float), kAlign);
+  pl->ws_bytes = off;
+  return PA_OK;
+}
+
+// Workgroups of the persistent decode launch: as many as are resident at once.
+// Cached per (device, kernel instance) after the first query.
+std::atomic<int> g_grid_cache[16][3][2][4];
+
+pa_status decode_grid(int dtype, int D, int bs, int* grid) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  const int bi = bs == 4 ? 0 : bs == 8 ? 1 : bs == 16 ? 2 : 3;
+  std::atomic<int>* slot = (dev >= 0 && dev < 16) ? &g_grid_cache[dev][dtype][D == 128][bi] : nullptr;
+  if (slot) {
+    const int cached = slot->load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *grid = cached;
+      return PA_OK;
+    }
   }
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+  e = pa::decode_blocks_per_cu(dtype, D, bs, &per_cu);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+  *grid = std::max(1, cus) * std::max(1, per_cu);
+  if (slot) slot->store(*grid, std::memory_order_relaxed);
   return PA_OK;
 }
 
@@ -124,41 +172,55 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (!aligned(block_tables, 4) || !aligned(seq_lens, 4))
     return fail(PA_ERR_INVALID_ARG, "block_tables and seq_lens must be 4-byte aligned");
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-  if (pl.ws_bytes) {
-    if (!ext->workspace || ext->workspace_bytes < pl.ws_bytes)
-      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.ws_bytes,
-                  ext->workspace ? ext->workspace_bytes : (size_t)0);
-    if (!aligned(ext->workspace, 16)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  }
+  if (!ext->workspace || ext->workspace_bytes < pl.ws_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.ws_bytes,
+                ext->workspace ? ext->workspace_bytes : (size_t)0);
+  if (!aligned(ext->workspace, 16)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  int grid = 0;
+  st = decode_grid(ext->dtype, ext->head_dim, block_size, &grid);
+  if (st != PA_OK) return st;
 
+  const int32_t S = ext->num_seqs, Hq = ext->num_q_heads, D = ext->head_dim;
+  const int64_t ht2 = (int64_t)num_kv_heads * pl.head_tiles;
+  char* ws = static_cast<char*>(ext->workspace);
   pa::DecodeParams p;
-  p.q = q;
-  p.k_cache = k_cache;
-  p.v_cache = v_cache;
-  p.block_tables = block_tables;
-  p.seq_lens = seq_lens;
-  p.out = out;
-  p.ws_o = pl.ws_bytes ? static_cast<float*>(ext->workspace) : nullptr;
-  p.ws_ml = pl.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(ext->workspace) + pl.ws_o_bytes)
-                        : nullptr;
   p.num_blocks = ext->num_blocks;
-  p.num_seqs = ext->num_seqs;
-  p.num_q_heads = ext->num_q_heads;
+  p.num_q_heads = Hq;
   p.num_kv_heads = num_kv_heads;
-  p.group = ext->num_q_heads / num_kv_heads;
+  p.group = Hq / num_kv_heads;
   p.head_tiles = pl.head_tiles;
   p.max_blocks = ext->max_blocks_per_seq;
   p.max_tokens = pl.max_tokens;
   p.part_tokens = pl.part_tokens;
   p.pmax = pl.pmax;
+  p.nodes = pl.nodes;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);  // log2(e)
+  p.queue = reinterpret_cast<int32_t*>(ws);
 
+  const size_t esz = ext->dtype == PA_F32 ? 4 : 2;
   hipStream_t stream = static_cast<hipStream_t>(ext->stream);
-  hipError_t e = pa::launch_decode_partitions(ext->dtype, ext->head_dim, block_size, p, stream);
-  if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-  if (pl.pmax > 1) {
-    e = pa::launch_decode_merge(ext->dtype, ext->head_dim, p, stream);
-    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  // one launch per slice of at most pl.slice sequences, in order on the stream
+  for (int32_t s0 = 0; s0 < S; s0 += pl.slice) {
+    const int32_t n = std::min(pl.slice, S - s0);
+    const size_t rows0 = (size_t)s0 * Hq;
+    p.q = static_cast<const char*>(q) + rows0 * D * esz;
+    p.out = static_cast<char*>(out) + rows0 * D * esz;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables + (size_t)s0 * ext->max_blocks_per_seq;
+    p.seq_lens = seq_lens + s0;
+    p.num_seqs = n;
+    p.node_count = reinterpret_cast<int32_t*>(ws + pl.off_node_count) + (size_t)s0 * ht2 * pl.nodes;
+    p.root_count = reinterpret_cast<int32_t*>(ws + pl.off_root_count) + (size_t)s0 * ht2;
+    p.part_o = reinterpret_cast<float*>(ws + pl.off_part_o) + rows0 * pl.pmax * D;
+    p.part_ml = reinterpret_cast<float*>(ws + pl.off_part_ml) + rows0 * pl.pmax * 2;
+    p.node_o = reinterpret_cast<float*>(ws + pl.off_node_o) + rows0 * pl.nodes * D;
+    p.node_ml = reinterpret_cast<float*>(ws + pl.off_node_ml) + rows0 * pl.nodes * 2;
+    // no more workgroups than there can be items
+    const int64_t most = (int64_t)n * pl.pmax * ht2;
+    const int g = (int)std::min<int64_t>(grid, most);
+    const hipError_t e = pa::launch_decode(ext->dtype, D, block_size, p, g, stream);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   }
   return PA_OK;
 }

@@ -49,17 +49,44 @@ def _ws(lib, ext, bs=16, hkv=8):
     return st, n.value
 
 
+def _layout(S, Hq, Hkv, D, pmax):
+    """Expected workspace bytes: [queue][group counters][root counters][partition
+    partials][group partials], each part rounded up to 256 bytes."""
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    tiles = (Hq // Hkv + 15) // 16
+    nodes = (pmax + 15) // 16
+    n = 256
+    n = r(n + S * Hkv * tiles * nodes * 4)
+    n = r(n + S * Hkv * tiles * 4)
+    rows = S * Hq
+    if pmax > 1:
+        n = r(n + rows * pmax * D * 4)
+        n = r(n + rows * pmax * 2 * 4)
+    if nodes > 1:
+        n = r(n + rows * nodes * D * 4)
+        n = r(n + rows * nodes * 2 * 4)
+    return n
+
+
 def test_workspace_size_formula(lib):
-    # 8 seqs x 32 heads x 256 partitions x (128 + 2) floats, each part 256-byte aligned
+    # 8 seqs x 32 heads x 256 partitions of 512 tokens, 16 groups of 16 partitions
     st, n = _ws(lib, _ext())
-    rows = 8 * 32 * 256
-    assert st == B.PA_OK and n == rows * 128 * 4 + rows * 2 * 4
-    st, n = _ws(lib, _ext(partition_size=-1))          # never split
-    assert st == B.PA_OK and n == 0
+    assert st == B.PA_OK and n == _layout(8, 32, 8, 128, 256)
+    assert n >= 8 * 32 * 256 * 130 * 4 + 8 * 32 * 16 * 130 * 4
+    st, n = _ws(lib, _ext(partition_size=-1))          # never split: queue and counters only
+    assert st == B.PA_OK and n == _layout(8, 32, 8, 128, 1) and n < 4096
     st, n = _ws(lib, _ext(max_blocks_per_seq=32))      # 512 tokens fit one partition
-    assert st == B.PA_OK and n == 0
+    assert st == B.PA_OK and n == _layout(8, 32, 8, 128, 1)
     st, n = _ws(lib, _ext(partition_size=0))           # default is 512 tokens
-    assert st == B.PA_OK and n == rows * 130 * 4
+    assert st == B.PA_OK and n == _layout(8, 32, 8, 128, 256)
+    st, n = _ws(lib, _ext(max_blocks_per_seq=64))      # two partitions, one group
+    assert st == B.PA_OK and n == _layout(8, 32, 8, 128, 2)
+    st, n = _ws(lib, _ext(num_q_heads=64, num_seqs=3))  # group of 8 heads: one tile each
+    assert st == B.PA_OK and n == _layout(3, 64, 8, 128, 256)
+    st, n = _ws(lib, _ext(num_q_heads=40, num_seqs=3))  # group of 5 heads
+    assert st == B.PA_OK and n == _layout(3, 40, 8, 128, 256)
+    st, n = _ws(lib, _ext(num_q_heads=160, num_seqs=3))  # group of 20 heads: two tiles
+    assert st == B.PA_OK and n == _layout(3, 160, 8, 128, 256)
 
 
 @pytest.mark.parametrize("kw,bs,hkv,want", [
@@ -76,7 +103,8 @@ def test_workspace_size_formula(lib):
     (dict(num_seqs=70000), 16, 8, B.PA_ERR_INVALID_ARG),
     (dict(partition_size=100), 16, 8, B.PA_ERR_INVALID_ARG),  # not a multiple of 32
     (dict(partition_size=32, max_blocks_per_seq=1 << 20), 16, 8, B.PA_ERR_UNSUPPORTED),
-    (dict(), 16, 8, B.PA_ERR_WORKSPACE),                       # split needs a workspace
+    (dict(), 16, 8, B.PA_ERR_WORKSPACE),                       # every call needs one
+    (dict(partition_size=-1), 16, 8, B.PA_ERR_WORKSPACE),      # even without a split
     (dict(workspace=FAKE, workspace_bytes=1024), 16, 8, B.PA_ERR_WORKSPACE),
 ])
 def test_decode_rejects(lib, kw, bs, hkv, want):
