@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "attended KV tokens/s and achieved HBM GB/s (% of peak), decode, 1 MI355X"
 PEAK_GBPS = 8000.0  # MI355X HBM3E peak
 MALL_BYTES = 256 << 20
+CALIBRATION_BYTES = 256 << 20
 HEADLINE = "gqa_bf16"
 WORKLOAD_TEXT = {
     "gqa_bf16": "bf16 GQA decode step: 128 seqs, 64 q heads / 8 KV heads, head_dim 128, "
@@ -240,6 +241,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--also", default="long_bf16_bs16,long_bf16_bs32",
                     help="comma-separated secondary batches measured decode-only ('' for none)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one 256 MiB device-to-device copy, a dispatch of known size "
+                         "against which rocprofv3's FETCH_SIZE / WRITE_SIZE counters are scaled")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this library "
@@ -253,6 +257,15 @@ def main():
         return 1
     from paged_kv_cache_344_amd.binding import lib
     lib()
+    if args.calibrate_copy:
+        src = torch.ones(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {CALIBRATION_BYTES} bytes read and {CALIBRATION_BYTES} written")
+        del src, dst
+        torch.cuda.empty_cache()
 
     head = measure(HEADLINE, args.seed, args.steps, args.warmup, args.copies, with_write=True)
     b = head["batch"]
@@ -307,7 +320,8 @@ def main():
                    "rotated_copies": head["n_copies"], "parallelism": "1 GPU"},
         "roofline": {"bound": "hbm", "achieved": head["gbps"], "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": head["gbps"] / PEAK_GBPS, "traffic": traffic,
-                     "kernel": "pa_decode call (partition kernel + split-K merge kernel)",
+                     "kernel": "decode_kernel<bf16, D=128, bs=16>: one launch per pa_decode "
+                               "call (partitions and split-K merge in the same launch)",
                      "algorithmic_bytes_per_call": head["decode_bytes"],
                      "mean_call_us": head["decode_ms"] * 1e3,
                      "p10_call_us": head["decode_ms_p10"] * 1e3,
