@@ -122,29 +122,16 @@ __device__ __forceinline__ void store4(T* p, f32x4 v) {
 
 // Partial results cross workgroups (and XCDs, whose L2 caches are not coherent with
 // each other) inside one launch.  They are written and read with device-scope
-// accesses, which go to the device's coherence point instead of a private L2, so no
-// cache-wide write-back or invalidate is needed: a writer waits for its stores to
-// complete (vmcnt 0) before a barrier and the arrival count; a reader that saw the
-// count complete reads with device-scope loads.
-__device__ __forceinline__ void st_dev(float* p, f32x4 v) {
-  const u32x4 u = __builtin_bit_cast(u32x4, v);
-  uint64_t* q = reinterpret_cast<uint64_t*>(p);
-  __hip_atomic_store(q, (uint64_t)u[0] | ((uint64_t)u[1] << 32), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, (uint64_t)u[2] | ((uint64_t)u[3] << 32), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
+// accesses (the sc1 cache policy), which go to the device's coherence point instead
+// of a private L2, so no cache-wide write-back or invalidate is needed: a writer waits
+// for its stores to complete (vmcnt 0) before a barrier and the arrival count; a
+// reader that saw the count complete reads with device-scope loads.  Rows are moved
+// as whole 16-byte pieces through buffer instructions, whose base must be
+// wave-uniform and whose offset is 32-bit.
 __device__ __forceinline__ void st_dev2(float* p, float a, float b) {
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p),
                      (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32),
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ f32x4 ld_dev(const float* p) {
-  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __builtin_bit_cast(f32x4, u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b,
-                                         (uint32_t)(b >> 32)});
 }
 // (max, sum) pair of one partial
 __device__ __forceinline__ void ld_dev2(const float* p, float& a, float& b) {
@@ -152,6 +139,16 @@ __device__ __forceinline__ void ld_dev2(const float* p, float& a, float& b) {
                                        __HIP_MEMORY_SCOPE_AGENT);
   a = __uint_as_float((uint32_t)v);
   b = __uint_as_float((uint32_t)(v >> 32));
+}
+// 16-byte device-scope store / load at byte offset `off` (< 2^31) from a wave-uniform base
+__device__ __forceinline__ void st_dev16(float* base, int off, f32x4 v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 16);
+}
+__device__ __forceinline__ f32x4 ld_dev16(const float* base, int off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, 0x00020000);
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
 }
 // every store this wave has issued is complete (and, device-scope, visible device-wide)
 __device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -208,20 +205,21 @@ __device__ __forceinline__ f32x4 qk_tile(const u32x4 (&k)[Chunk<T, D>::KL],
 template <typename T, int D>
 __device__ void merge_partials(const float* src_o, const float* src_ml, int64_t row0, int stride,
                                int first, int cnt, int nh, T* out, float* dst_o, float* dst_ml,
-                               int dstride, int dslot) {
+                               int dstride, int dslot, int Hq) {
   constexpr int C4 = D / 4;
   for (int it = threadIdx.x; it < nh * C4; it += NT_THREADS) {
     const int hh = it / C4, c = it - hh * C4;
-    const int64_t base = (row0 + hh) * stride + first;
+    // partial slots are [sequence][partition][query head]
+    const int64_t sq = row0 / Hq, h = row0 - sq * Hq + hh;
+    const int64_t base = (sq * stride + first) * Hq + h;
     const float* ml = src_ml + 2 * base;
-    const float* o = src_o + base * D + 4 * c;
     // Loads go out in batches of 8 before any is used: device-scope loads keep
     // program order, so a use right after each load would wait on each one.
     float M = -INFINITY;
     for (int i0 = 0; i0 < cnt; i0 += 8) {
       float mv[8], lv[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) ld_dev2(ml + 2 * min(i0 + k, cnt - 1), mv[k], lv[k]);
+      for (int k = 0; k < 8; ++k) ld_dev2(ml + 2 * (int64_t)min(i0 + k, cnt - 1) * Hq, mv[k], lv[k]);
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         if (i0 + k < cnt) M = fmaxf(M, mv[k]);
@@ -234,8 +232,8 @@ __device__ void merge_partials(const float* src_o, const float* src_ml, int64_t 
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int i = min(i0 + k, cnt - 1);
-        ld_dev2(ml + 2 * i, mv[k], lv[k]);
-        ov[k] = ld_dev(o + (int64_t)i * D);
+        ld_dev2(ml + 2 * (int64_t)i * Hq, mv[k], lv[k]);
+        ov[k] = ld_dev16(src_o + (sq * stride + first + i) * Hq * D, (int)((row0 - sq * Hq + hh) * D + 4 * c) * 4);
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -249,8 +247,8 @@ __device__ void merge_partials(const float* src_o, const float* src_ml, int64_t 
     if (out) {
       store4(out + (row0 + hh) * D + 4 * c, O / Ls);
     } else {
-      const int64_t d = (row0 + hh) * dstride + dslot;
-      st_dev(dst_o + d * D + 4 * c, O);
+      const int64_t d = (sq * dstride + dslot) * Hq + h;
+      st_dev16(dst_o + (sq * dstride + dslot) * Hq * D, (int)((row0 - sq * Hq + hh) * D + 4 * c) * 4, O);
       if (c == 0) st_dev2(dst_ml + 2 * d, M, Ls);
     }
   }
@@ -652,8 +650,9 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
         if (n == 1) {
           store4((T*)P.out + (row0 + hh) * D + d4, O / Ls);
         } else {
-          const int64_t slot = (row0 + hh) * P.pmax + p;
-          st_dev(P.part_o + slot * D + d4, O);
+          const int64_t slot = ((int64_t)s * P.pmax + p) * Hq + hbase + hh;
+          // the item's rows are contiguous: one wave-uniform base, 32-bit offsets
+          st_dev16(P.part_o + ((int64_t)s * P.pmax + p) * Hq * D, (int)((hbase + hh) * D + d4) * 4, O);
           if (d4 == 0) st_dev2(P.part_ml + 2 * slot, M, Ls);
         }
       }
@@ -676,10 +675,10 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
         if (sm_flag[0]) {
           if (ngrp == 1) {
             merge_partials<T, D>(P.part_o, P.part_ml, row0, P.pmax, 0, n, nh, (T*)P.out,
-                                 nullptr, nullptr, 0, 0);
+                                 nullptr, nullptr, 0, 0, Hq);
           } else {
             merge_partials<T, D>(P.part_o, P.part_ml, row0, P.pmax, grp * kMergeFan, gsize, nh,
-                                 (T*)nullptr, P.node_o, P.node_ml, P.nodes, grp);
+                                 (T*)nullptr, P.node_o, P.node_ml, P.nodes, grp, Hq);
             stores_done();
             __syncthreads();
             if (tid == 0) {
@@ -692,7 +691,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
             __syncthreads();
             if (sm_flag[1]) {
               merge_partials<T, D>(P.node_o, P.node_ml, row0, P.nodes, 0, ngrp, nh, (T*)P.out,
-                                   nullptr, nullptr, 0, 0);
+                                   nullptr, nullptr, 0, 0, Hq);
             }
           }
         }

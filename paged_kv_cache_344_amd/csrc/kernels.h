@@ -23,10 +23,10 @@ struct DecodeParams {
   const int32_t* block_tables;  // [S][max_blocks]
   const int32_t* seq_lens;      // [S]
   void* out;                    // [S][Hq][D]
-  float* part_o;                // [S][Hq][pmax][D]   per-partition unnormalised outputs
-  float* part_ml;               // [S][Hq][pmax][2]   (running max in log2 units, sum)
-  float* node_o;                // [S][Hq][nodes][D]  merged groups of kMergeFan partitions
-  float* node_ml;               // [S][Hq][nodes][2]
+  float* part_o;                // [S][pmax][Hq][D]   per-partition unnormalised outputs
+  float* part_ml;               // [S][pmax][Hq][2]   (running max in log2 units, sum)
+  float* node_o;                // [S][nodes][Hq][D]  merged groups of kMergeFan partitions
+  float* node_ml;               // [S][nodes][Hq][2]
   int32_t* queue;               // [2]: next work item, finished workgroups (0 between calls)
   int32_t* node_count;          // [S][Hkv*tiles][nodes]: partitions finished per group
   int32_t* root_count;          // [S][Hkv*tiles]: groups finished per sequence and head tile

@@ -96,7 +96,8 @@ pa_status plan_decode(const pa_decode_ext* ext, int32_t bs, int32_t hkv, Plan* p
   pl->head_tiles = tiles;
   pl->max_tokens = (int32_t)max_tokens;
   pl->slice = (int32_t)slice;
-  // [queue: 2 ints][node counts][root counts][partition partials][group partials]
+  // [queue: 2 ints][node counts][root counts][partition partials][group partials];
+  // partials are [sequence][partition or group][query head][D] (and [..][2] for max, sum)
   size_t off = kAlign;
   pl->off_node_count = off;
   off = round_up(off + (size_t)S * ht2 * nodes * sizeof(int32_t), kAlign);
