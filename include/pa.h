@@ -62,7 +62,8 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARG = 1, /* a null pointer, a bad size, a misaligned pointer       */
   PA_ERR_UNSUPPORTED = 2, /* valid but not built: dtype / head_dim / block_size ... */
   PA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required       */
-  PA_ERR_HIP = 4          /* the HIP runtime refused a launch; see pa_last_error()   */
+  PA_ERR_HIP = 4,         /* the HIP runtime refused a launch; see pa_last_error()   */
+  PA_ERR_CAPACITY = 5     /* block manager: no free block, or a table would overflow */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -185,6 +186,41 @@ typedef struct pa_cache_write_ext {
  */
 pa_status pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
                          void* k_cache, void* v_cache, const pa_cache_write_ext* ext);
+
+/* Shapes of a pa_copy_blocks call. */
+typedef struct pa_copy_blocks_ext {
+  int32_t num_kv_heads; /* Hkv > 0                                   */
+  int32_t head_dim;     /* D > 0, a multiple of 8                    */
+  int32_t block_size;   /* bs: 4, 8, 16 or 32                        */
+  int64_t num_blocks;   /* N >= 1                                    */
+  int32_t dtype;        /* pa_dtype of the caches                    */
+  void* stream;         /* hipStream_t                               */
+} pa_copy_blocks_ext;
+
+/*
+ * pa_copy_blocks - copy whole physical blocks of both caches (copy-on-write).
+ *
+ * For every i < n, block dst[i] of k_cache and of v_cache becomes a bit copy of
+ * block src[i]: every KV head and every slot.  A sequence about to write into a
+ * block that other sequences share gets a private copy first ([CY] 多序列共享;
+ * [ASP] 实现要点); pa_bm_append (pa_block_manager.h) names the copies to make.
+ *
+ *   k_cache, v_cache   device, layouts as in pa_decode
+ *   src, dst           HOST int32 arrays [n], each entry in [0, N); src[i] != dst[i];
+ *                      destinations distinct and none of them a source
+ *
+ * The index arrays are read during the call (copied into the launch arguments,
+ * 128 pairs a launch), so the caller may reuse them as soon as it returns, and the
+ * call needs no device memory of its own.  Asynchronous on ext->stream.
+ *
+ * Errors: PA_ERR_INVALID_ARG for a NULL ext or pointer (when n > 0), caches not
+ * 16-byte aligned, bad shapes or dtype, an id outside [0, N), src[i] == dst[i], a
+ * repeated destination or a destination that is also a source -- all found before
+ * anything is launched; PA_ERR_UNSUPPORTED for a block size not built; PA_ERR_HIP
+ * if a launch fails (launches before it may have run).  n == 0 does nothing.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                         int32_t n, const pa_copy_blocks_ext* ext);
 
 /* Static text for a status code. */
 const char* pa_status_string(pa_status status);

@@ -14,7 +14,7 @@ import torch
 
 from .build import LIB_PATH, INCLUDE
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_CAPACITY = range(6)
 PA_F32, PA_F16, PA_BF16 = range(3)
 TORCH_DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
@@ -40,6 +40,12 @@ class CacheWriteExt(ctypes.Structure):
                 ("stream", ctypes.c_void_p)]
 
 
+class CopyBlocksExt(ctypes.Structure):
+    _fields_ = [("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("stream", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -60,6 +66,24 @@ def lib():
         L.pa_decode_workspace_bytes.restype = ctypes.c_int
         L.pa_cache_write.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(CacheWriteExt)]
         L.pa_cache_write.restype = ctypes.c_int
+        L.pa_copy_blocks.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(CopyBlocksExt)]
+        L.pa_copy_blocks.restype = ctypes.c_int
+        P32, P64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+        L.pa_bm_create.argtypes = [ctypes.c_int64, i32, i32, vp, ctypes.POINTER(vp)]
+        L.pa_bm_destroy.argtypes = [vp]
+        L.pa_bm_destroy.restype = None
+        L.pa_bm_add_sequence.argtypes = [vp, P32]
+        L.pa_bm_fork.argtypes = [vp, i32, P32]
+        L.pa_bm_free_sequence.argtypes = [vp, i32]
+        L.pa_bm_append.argtypes = [vp, vp, i32, vp, vp, vp, P32]
+        L.pa_bm_length.argtypes = [vp, i32, P32]
+        L.pa_bm_export.argtypes = [vp, vp, i32, vp, vp]
+        L.pa_bm_free_blocks.argtypes = [vp]
+        L.pa_bm_free_blocks.restype = ctypes.c_int64
+        L.pa_bm_ref_count.argtypes = [vp, i32, P32]
+        for f in ("pa_bm_create", "pa_bm_add_sequence", "pa_bm_fork", "pa_bm_free_sequence",
+                  "pa_bm_append", "pa_bm_length", "pa_bm_export", "pa_bm_ref_count"):
+            getattr(L, f).restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_last_error.argtypes = []
@@ -70,11 +94,18 @@ def lib():
     return _lib
 
 
+HEADERS = ("pa.h", "pa_block_manager.h")
+
+
 def header_functions() -> list:
-    """Names of the functions include/pa.h declares."""
-    text = open(os.path.join(INCLUDE, "pa.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:pa_status|const char\s*\*|int32_t|size_t)\s+(pa_\w+)\s*\(",
-                                 text, re.M)))
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for h in HEADERS:
+        text = open(os.path.join(INCLUDE, h)).read()
+        names |= set(re.findall(
+            r"^\s*(?:pa_status|const char\s*\*|int32_t|int64_t|size_t|void)\s+(pa_\w+)\s*\(",
+            text, re.M))
+    return sorted(names)
 
 
 def _check(status: int, where: str):
@@ -235,3 +266,123 @@ def pa_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     """Store new tokens' K/V in their slots (see include/pa.h).  k, v [T, Hkv, D];
     slot_mapping int64 [T]; caches as for pa_decode."""
     PreparedCacheWrite(k, v, slot_mapping, k_cache, v_cache, stream=stream)()
+
+
+class PreparedCopyBlocks:
+    """A pa_copy_blocks call with all marshalling done once (see PreparedDecode).
+    ``src`` and ``dst`` are host sequences of block ids; the ids travel to the GPU
+    inside the kernel arguments, so the call needs no device memory of its own."""
+
+    def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, src, dst, *,
+                 stream=None):
+        dev = k_cache.device
+        _need(dev.type == "cuda", "caches must be on a GPU")
+        _need(v_cache.device == dev, f"v_cache is on {v_cache.device}, k_cache on {dev}")
+        _need(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+        _need(k_cache.dtype in TORCH_DTYPE and v_cache.dtype == k_cache.dtype,
+              "k_cache and v_cache must share one supported dtype")
+        N, Hkv, bs, D = k_cache.shape
+        _need(v_cache.shape == (N, Hkv, D, bs), f"v_cache shape {tuple(v_cache.shape)}")
+        src, dst = [int(x) for x in src], [int(x) for x in dst]
+        _need(len(src) == len(dst), "src and dst differ in length")
+        n = len(src)
+        self.src = (ctypes.c_int32 * max(n, 1))(*src)
+        self.dst = (ctypes.c_int32 * max(n, 1))(*dst)
+        self.ext = CopyBlocksExt(num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=N,
+                                 dtype=TORCH_DTYPE[k_cache.dtype],
+                                 stream=_stream_ptr(dev, stream))
+        self.tensors = (k_cache, v_cache)
+        self._fn = lib().pa_copy_blocks
+        self._args = (k_cache.data_ptr(), v_cache.data_ptr(), self.src, self.dst, n,
+                      ctypes.byref(self.ext))
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != PA_OK:
+            _check(st, "pa_copy_blocks")
+
+
+def pa_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src, dst, *,
+                   stream=None) -> None:
+    """Copy whole physical blocks of both caches, block src[i] onto block dst[i]
+    (see include/pa.h): the device half of copy-on-write."""
+    PreparedCopyBlocks(k_cache, v_cache, src, dst, stream=stream)()
+
+
+class BlockManager:
+    """The host block manager of include/pa_block_manager.h: one C object per
+    instance, freed with the instance (or by ``close()``)."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_blocks_per_seq: int,
+                 free_order=None):
+        L = lib()
+        self._L = L
+        self.block_size = block_size
+        self.max_blocks = max_blocks_per_seq
+        order = None
+        if free_order is not None:
+            free_order = [int(x) for x in free_order]
+            _need(len(free_order) == num_blocks, "free_order must list every block once")
+            order = (ctypes.c_int32 * num_blocks)(*free_order)
+        h = ctypes.c_void_p()
+        _check(L.pa_bm_create(num_blocks, block_size, max_blocks_per_seq, order,
+                              ctypes.byref(h)), "pa_bm_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._L.pa_bm_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add_sequence(self) -> int:
+        out = ctypes.c_int32()
+        _check(self._L.pa_bm_add_sequence(self._h, ctypes.byref(out)), "pa_bm_add_sequence")
+        return out.value
+
+    def fork(self, parent: int) -> int:
+        out = ctypes.c_int32()
+        _check(self._L.pa_bm_fork(self._h, parent, ctypes.byref(out)), "pa_bm_fork")
+        return out.value
+
+    def free_sequence(self, seq: int) -> None:
+        _check(self._L.pa_bm_free_sequence(self._h, seq), "pa_bm_free_sequence")
+
+    def append(self, seqs):
+        """One token for each of ``seqs``: returns (slot ids, [(src, dst) copies])."""
+        seqs = [int(x) for x in seqs]
+        n = len(seqs)
+        m = max(n, 1)
+        ids = (ctypes.c_int32 * m)(*seqs)
+        slots = (ctypes.c_int64 * m)()
+        cs, cd = (ctypes.c_int32 * m)(), (ctypes.c_int32 * m)()
+        nc = ctypes.c_int32()
+        _check(self._L.pa_bm_append(self._h, ids, n, slots, cs, cd, ctypes.byref(nc)),
+               "pa_bm_append")
+        return list(slots[:n]), [(cs[i], cd[i]) for i in range(nc.value)]
+
+    def length(self, seq: int) -> int:
+        out = ctypes.c_int32()
+        _check(self._L.pa_bm_length(self._h, seq, ctypes.byref(out)), "pa_bm_length")
+        return out.value
+
+    def export(self, seqs):
+        """(block tables [n][max_blocks] padded with -1, lengths [n]) as int32 CPU tensors."""
+        seqs = [int(x) for x in seqs]
+        n = len(seqs)
+        ids = (ctypes.c_int32 * max(n, 1))(*seqs)
+        bt = torch.empty((n, self.max_blocks), dtype=torch.int32)
+        sl = torch.empty((n,), dtype=torch.int32)
+        _check(self._L.pa_bm_export(self._h, ids, n, bt.data_ptr() if n else None,
+                                    sl.data_ptr() if n else None), "pa_bm_export")
+        return bt, sl
+
+    def free_blocks(self) -> int:
+        return int(self._L.pa_bm_free_blocks(self._h))
+
+    def ref_count(self, block: int) -> int:
+        out = ctypes.c_int32()
+        _check(self._L.pa_bm_ref_count(self._h, block, ctypes.byref(out)), "pa_bm_ref_count")
+        return out.value

@@ -57,6 +57,16 @@ struct CacheWriteParams {
   int32_t block_size;
 };
 
+constexpr int kCopyBatch = 128;  // block copies per launch (their ids travel as arguments)
+
+struct CopyBlocksParams {
+  char* k_cache;
+  char* v_cache;
+  int64_t block_bytes;  // Hkv * bs * D * element size: one physical block of one cache
+  int32_t n;            // pairs in this launch
+  int32_t pairs[2 * kCopyBatch];  // (src, dst) block ids
+};
+
 // dtype codes follow pa_dtype: 0 f32, 1 f16, 2 bf16.
 // Each returns hipErrorInvalidValue for a (dtype, head_dim, block_size) that has
 // no compiled instance; the caller checks support first.
@@ -65,5 +75,6 @@ hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodePa
 // Workgroups of the decode kernel that fit on one compute unit at once.
 hipError_t decode_blocks_per_cu(int dtype, int head_dim, int block_size, int* blocks);
 hipError_t launch_cache_write(int elem_bytes, const CacheWriteParams& p, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
 
 }  // namespace pa

@@ -12,6 +12,7 @@
 #include <atomic>
 #include <cmath>
 #include <string>
+#include <vector>
 
 #include "kernels.h"
 #include "pa.h"
@@ -265,6 +266,63 @@ pa_status pa_cache_write(const void* k, const void* v, const int64_t* slot_mappi
   return PA_OK;
 }
 
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                         int32_t n, const pa_copy_blocks_ext* ext) {
+  g_error.clear();
+  if (!ext) return fail(PA_ERR_INVALID_ARG, "ext is NULL");
+  const int32_t Hkv = ext->num_kv_heads, D = ext->head_dim, bs = ext->block_size;
+  if (n < 0) return fail(PA_ERR_INVALID_ARG, "n %d < 0", n);
+  if (Hkv <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d <= 0", Hkv);
+  if (D <= 0 || D % 8) return fail(PA_ERR_INVALID_ARG, "head_dim %d is not a positive multiple of 8", D);
+  if (bs <= 0) return fail(PA_ERR_INVALID_ARG, "block_size %d <= 0", bs);
+  if (!block_size_built(bs)) return fail(PA_ERR_UNSUPPORTED, "block_size %d (built: 4, 8, 16, 32)", bs);
+  if (ext->num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks %lld <= 0", (long long)ext->num_blocks);
+  if (!dtype_valid(ext->dtype)) return fail(PA_ERR_INVALID_ARG, "dtype %d", ext->dtype);
+  if (n == 0) return PA_OK;
+  if (!k_cache || !v_cache || !src || !dst) return fail(PA_ERR_INVALID_ARG, "a pointer is NULL");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(PA_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+  // ids in the pool, no self-copy, destinations distinct and never a source (a copy
+  // must not read a block another copy of the same call writes)
+  std::vector<int32_t> ds(dst, dst + n), ss(src, src + n);
+  for (int32_t i = 0; i < n; ++i) {
+    if (src[i] < 0 || src[i] >= ext->num_blocks || dst[i] < 0 || dst[i] >= ext->num_blocks)
+      return fail(PA_ERR_INVALID_ARG, "pair %d (%d -> %d) outside the pool", i, src[i], dst[i]);
+    if (src[i] == dst[i]) return fail(PA_ERR_INVALID_ARG, "pair %d copies block %d onto itself", i, src[i]);
+  }
+  std::sort(ds.begin(), ds.end());
+  std::sort(ss.begin(), ss.end());
+  for (int32_t i = 1; i < n; ++i)
+    if (ds[(size_t)i] == ds[(size_t)i - 1]) return fail(PA_ERR_INVALID_ARG, "block %d is a destination twice", ds[(size_t)i]);
+  for (size_t i = 0, j = 0; i < ds.size() && j < ss.size();) {
+    if (ds[i] == ss[j]) return fail(PA_ERR_INVALID_ARG, "block %d is both a source and a destination", ds[i]);
+    if (ds[i] < ss[j]) ++i;
+    else ++j;
+  }
+  pa::CopyBlocksParams p;
+  p.k_cache = static_cast<char*>(k_cache);
+  p.v_cache = static_cast<char*>(v_cache);
+  p.block_bytes = (int64_t)Hkv * bs * D * (ext->dtype == PA_F32 ? 4 : 2);
+  hipStream_t stream = static_cast<hipStream_t>(ext->stream);
+  for (int32_t i0 = 0; i0 < n; i0 += pa::kCopyBatch) {
+    p.n = std::min(pa::kCopyBatch, n - i0);
+    for (int32_t i = 0; i < p.n; ++i) {
+      p.pairs[2 * i] = src[i0 + i];
+      p.pairs[2 * i + 1] = dst[i0 + i];
+    }
+    const hipError_t e = pa::launch_copy_blocks(p, stream);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "copy launch: %s", hipGetErrorString(e));
+  }
+  return PA_OK;
+}
+
+__attribute__((visibility("hidden"))) void pa_set_last_error_internal(const char* text) {
+  try {
+    g_error = text ? text : "";
+  } catch (...) {
+  }
+}
+
 const char* pa_status_string(pa_status status) {
   switch (status) {
     case PA_OK: return "ok";
@@ -272,6 +330,7 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_CAPACITY: return "no free block, or a block table would overflow";
   }
   return "unknown status";
 }

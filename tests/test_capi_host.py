@@ -25,8 +25,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for st in range(5):
-        assert lib.pa_status_string(st)
+    for st in range(6):
+        assert lib.pa_status_string(st) != b"unknown status"
     assert lib.pa_status_string(99) == b"unknown status"
 
 
@@ -158,3 +158,44 @@ def test_last_error_clears_on_success(lib):
     assert _cw(lib, num_blocks=0) != B.PA_OK and lib.pa_last_error()
     assert _cw(lib, ptr=0, num_tokens=0) == B.PA_OK
     assert lib.pa_last_error() == b""
+
+
+def _cb(lib, src, dst, ptr=FAKE, ext=True, **kw):
+    base = dict(num_kv_heads=8, head_dim=128, block_size=16, num_blocks=100,
+                dtype=B.PA_BF16, stream=None)
+    base.update(kw)
+    e = B.CopyBlocksExt(**base)
+    n = len(src)
+    s = (ctypes.c_int32 * max(n, 1))(*src)
+    d = (ctypes.c_int32 * max(n, 1))(*dst)
+    return lib.pa_copy_blocks(ptr, ptr, s, d, n, ctypes.byref(e) if ext else None)
+
+
+@pytest.mark.parametrize("src,dst,kw,want", [
+    ([1], [2], dict(num_kv_heads=0), B.PA_ERR_INVALID_ARG),
+    ([1], [2], dict(head_dim=100), B.PA_ERR_INVALID_ARG),
+    ([1], [2], dict(block_size=12), B.PA_ERR_UNSUPPORTED),
+    ([1], [2], dict(block_size=0), B.PA_ERR_INVALID_ARG),
+    ([1], [2], dict(num_blocks=0), B.PA_ERR_INVALID_ARG),
+    ([1], [2], dict(dtype=3), B.PA_ERR_INVALID_ARG),
+    ([1], [100], dict(), B.PA_ERR_INVALID_ARG),                 # outside the pool
+    ([-1], [2], dict(), B.PA_ERR_INVALID_ARG),
+    ([3], [3], dict(), B.PA_ERR_INVALID_ARG),                   # onto itself
+    ([1, 2], [5, 5], dict(), B.PA_ERR_INVALID_ARG),             # destination twice
+    ([1, 5], [5, 6], dict(), B.PA_ERR_INVALID_ARG),             # destination is a source
+    (list(range(0, 60)), list(range(60, 119)) + [0], dict(), B.PA_ERR_INVALID_ARG),
+])
+def test_copy_blocks_rejects(lib, src, dst, kw, want):
+    assert _cb(lib, src, dst, **kw) == want
+    assert lib.pa_last_error()
+
+
+def test_copy_blocks_pointer_checks(lib):
+    assert _cb(lib, [1], [2], ext=False) == B.PA_ERR_INVALID_ARG
+    assert _cb(lib, [1], [2], ptr=0) == B.PA_ERR_INVALID_ARG
+    assert _cb(lib, [1], [2], ptr=FAKE + 8) == B.PA_ERR_INVALID_ARG
+    e = B.CopyBlocksExt(num_kv_heads=8, head_dim=128, block_size=16, num_blocks=100,
+                        dtype=B.PA_BF16, stream=None)
+    assert lib.pa_copy_blocks(FAKE, FAKE, None, None, 1, ctypes.byref(e)) == B.PA_ERR_INVALID_ARG
+    assert lib.pa_copy_blocks(FAKE, FAKE, None, None, -1, ctypes.byref(e)) == B.PA_ERR_INVALID_ARG
+    assert _cb(lib, [], [], ptr=0) == B.PA_OK     # nothing to copy
