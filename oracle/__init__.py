@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for paged decode attention and the KV-cache write.
+"""fp64 CPU oracle for paged decode attention, attention for several new tokens per
+sequence, and the KV-cache write.
 
 TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, ``__graft_entry__.smoke()``
 and the CPU-baseline leg of ``bench.py`` may import this package.  The GPU library
@@ -65,6 +66,9 @@ def _load():
         lib.oracle_decode.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, i32,
                                       dbl, p]
         lib.oracle_decode.restype = ctypes.c_int
+        lib.oracle_multi_token.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
+                                           i64, i32, dbl, p]
+        lib.oracle_multi_token.restype = ctypes.c_int
         lib.oracle_cache_write.argtypes = [p, p, p, i32, i32, i32, i32, i64, i32, p, p]
         lib.oracle_cache_write.restype = ctypes.c_int
         lib.oracle_decode_elements.argtypes = [p, i64, i32, p]
@@ -126,6 +130,37 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, block_size: int, num_kv_
                                float(scale), _ptr(out))
     if rc != OK:
         raise OracleError(rc, "decode")
+    return out
+
+
+def multi_token(q, k_cache, v_cache, block_tables, seq_lens, query_start, block_size: int,
+                num_kv_heads: int, scale: float, dtype: str) -> np.ndarray:
+    """Reference attention for several new tokens per sequence; returns float64
+    [T, Hq, D].  q [T, Hq, D] holds sequence s's new tokens in rows
+    query_start[s] .. query_start[s+1]-1 (int32 [S+1], query_start[0] = 0); they are
+    the last n_s of its seq_lens[s] cached tokens, and token j sees positions
+    0 .. seq_lens[s] - n_s + j."""
+    q = _storage(q, dtype)
+    k_cache = _storage(k_cache, dtype)
+    v_cache = _storage(v_cache, dtype)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    T, Hq, D = q.shape
+    S = sl.shape[0]
+    N = k_cache.shape[0]
+    if k_cache.shape != (N, num_kv_heads, block_size, D):
+        raise ValueError(f"k_cache shape {k_cache.shape}")
+    if v_cache.shape != (N, num_kv_heads, D, block_size):
+        raise ValueError(f"v_cache shape {v_cache.shape}")
+    if bt.ndim != 2 or bt.shape[0] != S or qs.shape != (S + 1,):
+        raise ValueError("block_tables / query_start shape")
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    rc = _load().oracle_multi_token(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(sl),
+                                    _ptr(qs), S, T, Hq, num_kv_heads, D, block_size, bt.shape[1],
+                                    N, DTYPES[dtype], float(scale), _ptr(out))
+    if rc != OK:
+        raise OracleError(rc, "multi_token")
     return out
 
 

@@ -271,3 +271,109 @@ int oracle_cache_write(const void* k, const void* v, const int64_t* slot_mapping
   }
   return OR_OK;
 }
+
+/* ---- several new tokens per sequence ------------------------------------------ */
+
+/*
+ * Attention for a chunk of new tokens per sequence (a prompt chunk when a new
+ * sequence joins a step, or draft tokens to verify): [ASP] 实现要点 (continuous
+ * batching adds sequences every step) and 已知局限 (speculative decoding over the
+ * paged cache).  The formula is still the scaled dot-product attention the cache
+ * serves ([ASP] 引用本概念的论文, "Attention Is All You Need"), whose decoder lets a
+ * token see itself and every earlier token, never a later one.
+ *
+ * Sequence s has L_s tokens in the cache (seq_lens), the last n_s of them new, with
+ * n_s = query_start[s+1] - query_start[s]; its queries are rows query_start[s] ..
+ * query_start[s+1]-1 of q and out ([T][Hq][D]).  New token j (0-based) sits at
+ * position c_s + j, c_s = L_s - n_s, and attends to positions 0 .. c_s + j:
+ *   out[query_start[s]+j][h][:] = sum_t w_t V[t][:] / sum_t w_t,  t = 0 .. c_s + j,
+ *   w_t = exp(z_t - max_u z_u),  z_t = scale * <q[query_start[s]+j][h], K[t]>.
+ * With n_s = 1 this is oracle_decode.  query_start[0] = 0, query_start[S] = T,
+ * non-decreasing, n_s <= L_s.  Returns an OR_* code; on error nothing is written.
+ */
+int oracle_multi_token(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* seq_lens,
+                       const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                       int32_t dtype, double scale, double* out) {
+  const int S = num_seqs, T = num_tokens, Hq = num_q_heads, Hkv = num_kv_heads, D = head_dim;
+  const int bs = block_size, MB = max_blocks_per_seq;
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start || !out)
+    return OR_BAD_ARG;
+  if (S < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || MB < 0 || num_blocks < 0)
+    return OR_BAD_ARG;
+  if (Hq % Hkv != 0) return OR_BAD_ARG;
+  if (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16) return OR_BAD_ARG;
+  if (query_start[0] != 0 || query_start[S] != T) return OR_BAD_ARG;
+  const int G = Hq / Hkv;
+
+  for (int s = 0; s < S; ++s) {
+    const int L = seq_lens[s];
+    const int n = query_start[s + 1] - query_start[s];
+    if (n < 0) return OR_BAD_ARG;
+    if (L < 0 || (int64_t)L > (int64_t)MB * bs || n > L) return OR_BAD_LEN;
+    const int nb = (L + bs - 1) / bs;
+    for (int j = 0; j < nb; ++j) {
+      const int32_t b = block_tables[(int64_t)s * MB + j];
+      if (b < 0 || (int64_t)b >= num_blocks) return OR_BAD_BLOCK;
+    }
+  }
+
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t task = 0; task < (int64_t)S * Hkv; ++task) {
+    const int s = (int)(task / Hkv), g = (int)(task % Hkv);
+    const int L = seq_lens[s];
+    const int n = query_start[s + 1] - query_start[s];
+    if (n == 0) continue;
+    const int c = L - n;
+    double* K = (double*)malloc(sizeof(double) * (size_t)L * D);
+    double* V = (double*)malloc(sizeof(double) * (size_t)L * D);
+    double* z = (double*)malloc(sizeof(double) * (size_t)L);
+    if (!K || !V || !z) {
+      free(K);
+      free(V);
+      free(z);
+#pragma omp atomic write
+      failed = 1;
+      continue;
+    }
+    for (int t = 0; t < L; ++t) {
+      const int64_t blk = block_tables[(int64_t)s * MB + t / bs];
+      const int o = t % bs;
+      for (int d = 0; d < D; ++d) {
+        K[(int64_t)t * D + d] = load_elem(k_cache, kpos(blk, g, o, d, Hkv, bs, D), dtype);
+        V[(int64_t)t * D + d] = load_elem(v_cache, vpos(blk, g, o, d, Hkv, bs, D), dtype);
+      }
+    }
+    for (int j = 0; j < n; ++j) {
+      const int last = c + j; /* the newest position this token may see */
+      for (int h = g * G; h < (g + 1) * G; ++h) {
+        const int64_t qo = ((int64_t)(query_start[s] + j) * Hq + h) * D;
+        for (int t = 0; t <= last; ++t) {
+          double acc = 0.0;
+          for (int d = 0; d < D; ++d) acc += load_elem(q, qo + d, dtype) * K[(int64_t)t * D + d];
+          z[t] = scale * acc;
+        }
+        double m = z[0];
+        for (int t = 1; t <= last; ++t)
+          if (z[t] > m) m = z[t];
+        double Z = 0.0;
+        for (int t = 0; t <= last; ++t) {
+          z[t] = exp(z[t] - m);
+          Z += z[t];
+        }
+        for (int d = 0; d < D; ++d) {
+          double acc = 0.0;
+          for (int t = 0; t <= last; ++t) acc += z[t] * V[(int64_t)t * D + d];
+          out[qo + d] = acc / Z;
+        }
+      }
+    }
+    free(K);
+    free(V);
+    free(z);
+  }
+  return failed ? OR_NOMEM : OR_OK;
+}
