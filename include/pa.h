@@ -187,6 +187,59 @@ typedef struct pa_cache_write_ext {
 pa_status pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
                          void* k_cache, void* v_cache, const pa_cache_write_ext* ext);
 
+/* Shapes and options of a pa_multi_token call. */
+typedef struct pa_multi_token_ext {
+  int32_t num_seqs;           /* S >= 0 (0: nothing to do) and <= 65535               */
+  int32_t num_tokens;         /* T = query_start[S] >= 0: rows of q and out            */
+  int32_t max_query_len;      /* >= every n_s: sizes the launch (0: nothing to do)     */
+  int32_t num_q_heads;        /* Hq > 0, a multiple of num_kv_heads                    */
+  int32_t head_dim;           /* D: 64 or 128                                          */
+  int32_t max_blocks_per_seq; /* row stride of block_tables, >= 1                      */
+  int64_t num_blocks;         /* N, physical blocks in the pool, >= 1                  */
+  int32_t dtype;              /* pa_dtype of q, k_cache, v_cache and out               */
+  void* stream;               /* hipStream_t                                           */
+} pa_multi_token_ext;
+
+/*
+ * pa_multi_token - attention for several new tokens per sequence over the paged cache:
+ * a prompt chunk of a sequence that joins the batch, or draft tokens to verify
+ * ([ASP] 实现要点, continuous batching; 已知局限, speculative decoding).
+ *
+ * Sequence s has seq_lens[s] = L_s tokens in the cache, the last n_s of them new
+ * (their K/V already stored, e.g. by pa_cache_write).  Its new tokens' queries are
+ * rows query_start[s] .. query_start[s+1]-1 of q, n_s = query_start[s+1] -
+ * query_start[s].  New token j (0-based) sits at position L_s - n_s + j and attends
+ * to positions 0 .. L_s - n_s + j of the sequence: itself and everything before it,
+ * nothing after (the decoder attention of the scaled dot-product definition the cache
+ * serves, [ASP] 引用本概念的论文).  Per query head h (KV head h / (Hq / Hkv)):
+ *   out[row][h] = softmax_t(scale * <q[row][h], K_t>) . V, t over those positions.
+ * With every n_s = 1 this is pa_decode.
+ *
+ *   q, out        device, [T][Hq][D], dtype ext->dtype, 16-byte aligned
+ *   k_cache       device, [N][Hkv][bs][D];  v_cache  device, [N][Hkv][D][bs]
+ *   block_tables  device int32 [S][max_blocks_per_seq] (entries past a sequence's
+ *                 last block are never read)
+ *   seq_lens      device int32 [S]
+ *   query_start   device int32 [S+1], query_start[0] = 0, non-decreasing,
+ *                 query_start[S] = T
+ *   block_size    4, 8, 16 or 32;  scale  finite
+ *
+ * Device-side contract (not checked on the host, which never reads device memory):
+ * n_s <= max_query_len and n_s <= L_s <= max_blocks_per_seq * bs, table entries in
+ * use lie in [0, N).  A sequence whose query_start entries do not fit in [0, T] is
+ * skipped; one with n_s > L_s or L_s > max_blocks_per_seq * bs, or a bad table entry,
+ * gets NaN rows; rows past max_query_len are not written.
+ *
+ * One launch, asynchronous on ext->stream, no device memory of its own.  Errors:
+ * PA_ERR_INVALID_ARG for NULL or misaligned pointers, bad shapes or dtype, a
+ * non-finite scale; PA_ERR_UNSUPPORTED for a head_dim or block_size not built or a
+ * launch too large; PA_ERR_HIP if the launch fails.
+ */
+pa_status pa_multi_token(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens,
+                         const int32_t* query_start, int32_t block_size, int32_t num_kv_heads,
+                         float scale, void* out, const pa_multi_token_ext* ext);
+
 /* Shapes of a pa_copy_blocks call. */
 typedef struct pa_copy_blocks_ext {
   int32_t num_kv_heads; /* Hkv > 0                                   */

@@ -4,5 +4,6 @@ kernels) and a thin ctypes binding with the same entry-point names.
 Importing the package does not load the library; the first call does, and fails
 loudly when it has not been built."""
 from .binding import (BlockManager, PaError, PreparedCacheWrite,  # noqa: F401
-                      PreparedCopyBlocks, PreparedDecode, pa_cache_write, pa_copy_blocks,
-                      pa_decode, pa_decode_workspace_bytes, workspace_for)
+                      PreparedCopyBlocks, PreparedDecode, PreparedMultiToken, pa_cache_write,
+                      pa_copy_blocks, pa_decode, pa_decode_workspace_bytes, pa_multi_token,
+                      workspace_for)

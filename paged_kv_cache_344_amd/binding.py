@@ -40,6 +40,14 @@ class CacheWriteExt(ctypes.Structure):
                 ("stream", ctypes.c_void_p)]
 
 
+class MultiTokenExt(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("max_query_len", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("stream", ctypes.c_void_p)]
+
+
 class CopyBlocksExt(ctypes.Structure):
     _fields_ = [("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int64),
@@ -66,6 +74,9 @@ def lib():
         L.pa_decode_workspace_bytes.restype = ctypes.c_int
         L.pa_cache_write.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(CacheWriteExt)]
         L.pa_cache_write.restype = ctypes.c_int
+        L.pa_multi_token.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp,
+                                     ctypes.POINTER(MultiTokenExt)]
+        L.pa_multi_token.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(CopyBlocksExt)]
         L.pa_copy_blocks.restype = ctypes.c_int
         P32, P64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -266,6 +277,66 @@ def pa_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     """Store new tokens' K/V in their slots (see include/pa.h).  k, v [T, Hkv, D];
     slot_mapping int64 [T]; caches as for pa_decode."""
     PreparedCacheWrite(k, v, slot_mapping, k_cache, v_cache, stream=stream)()
+
+
+class PreparedMultiToken:
+    """A pa_multi_token call with all marshalling done once (see PreparedDecode)."""
+
+    def __init__(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 block_tables: torch.Tensor, seq_lens: torch.Tensor, query_start: torch.Tensor,
+                 block_size: int, num_kv_heads: int, scale: float, out: torch.Tensor, *,
+                 max_query_len: int, stream=None):
+        dev = q.device
+        _need(dev.type == "cuda", "tensors must be on a GPU")
+        for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                        ("block_tables", block_tables), ("seq_lens", seq_lens),
+                        ("query_start", query_start), ("out", out)):
+            _need(t.device == dev, f"{name} is on {t.device}, q on {dev}")
+            _need(t.is_contiguous(), f"{name} must be contiguous")
+        _need(q.dtype in TORCH_DTYPE, f"unsupported dtype {q.dtype}")
+        _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype and out.dtype == q.dtype,
+              "q, k_cache, v_cache and out must share one dtype")
+        _need(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32 and
+              query_start.dtype == torch.int32, "block_tables, seq_lens, query_start must be int32")
+        T, Hq, D = q.shape
+        S = seq_lens.shape[0]
+        N = k_cache.shape[0]
+        _need(k_cache.shape == (N, num_kv_heads, block_size, D),
+              f"k_cache shape {tuple(k_cache.shape)}")
+        _need(v_cache.shape == (N, num_kv_heads, D, block_size),
+              f"v_cache shape {tuple(v_cache.shape)}")
+        _need(block_tables.dim() == 2 and block_tables.shape[0] == S, "block_tables shape")
+        _need(query_start.shape == (S + 1,), "query_start shape")
+        _need(out.shape == q.shape, "out shape")
+        self.ext = MultiTokenExt(num_seqs=S, num_tokens=T, max_query_len=max_query_len,
+                                 num_q_heads=Hq, head_dim=D,
+                                 max_blocks_per_seq=block_tables.shape[1], num_blocks=N,
+                                 dtype=TORCH_DTYPE[q.dtype], stream=_stream_ptr(dev, stream))
+        self.tensors = (q, k_cache, v_cache, block_tables, seq_lens, query_start, out)
+        self.out = out
+        self._fn = lib().pa_multi_token
+        self._args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                      block_tables.data_ptr(), seq_lens.data_ptr(), query_start.data_ptr(),
+                      block_size, num_kv_heads, ctypes.c_float(scale), out.data_ptr(),
+                      ctypes.byref(self.ext))
+
+    def __call__(self) -> torch.Tensor:
+        st = self._fn(*self._args)
+        if st != PA_OK:
+            _check(st, "pa_multi_token")
+        return self.out
+
+
+def pa_multi_token(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_tables: torch.Tensor, seq_lens: torch.Tensor, query_start: torch.Tensor,
+                   block_size: int, num_kv_heads: int, scale: float, out: torch.Tensor, *,
+                   max_query_len: int, stream=None) -> torch.Tensor:
+    """Attention for several new tokens per sequence (see include/pa.h): q, out
+    [T, Hq, D]; query_start int32 [S+1] on the GPU; ``max_query_len`` >= every
+    sequence's number of new tokens (a host value: it sizes the launch)."""
+    return PreparedMultiToken(q, k_cache, v_cache, block_tables, seq_lens, query_start,
+                              block_size, num_kv_heads, scale, out,
+                              max_query_len=max_query_len, stream=stream)()
 
 
 class PreparedCopyBlocks:

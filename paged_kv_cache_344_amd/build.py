@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libpa.so")
-SOURCES = ["decode.hip", "cache_write.hip", "copy_blocks.hip", "pa_api.cpp", "block_manager.cpp"]
+SOURCES = ["decode.hip", "cache_write.hip", "copy_blocks.hip", "multi_token.hip", "pa_api.cpp", "block_manager.cpp"]
 
 
 def hipcc() -> str:

@@ -57,6 +57,28 @@ struct CacheWriteParams {
   int32_t block_size;
 };
 
+// A pa_multi_token launch: rows are (new token, query head) pairs of one KV head.
+struct MultiTokenParams {
+  const void* q;                // [T][Hq][D]
+  const void* k_cache;          // [N][Hkv][bs][D]
+  const void* v_cache;          // [N][Hkv][D][bs]
+  const int32_t* block_tables;  // [S][max_blocks]
+  const int32_t* seq_lens;      // [S]: cached tokens, the new ones included
+  const int32_t* query_start;   // [S+1]: sequence s's new tokens are q rows qs[s] .. qs[s+1]-1
+  void* out;                    // [T][Hq][D]
+  int64_t num_blocks;           // N
+  int32_t num_seqs;             // S
+  int32_t num_tokens;           // T
+  int32_t num_q_heads;          // Hq
+  int32_t num_kv_heads;         // Hkv
+  int32_t group;                // Hq / Hkv
+  int32_t max_blocks;           // row stride of block_tables
+  int32_t max_tokens;           // max_blocks * bs
+  int32_t row_tiles;            // workgroup row tiles per (sequence, KV head)
+  int32_t per_xcd;              // set by the launcher
+  float scale_log2;             // scale * log2(e)
+};
+
 constexpr int kCopyBatch = 128;  // block copies per launch (their ids travel as arguments)
 
 struct CopyBlocksParams {
@@ -76,5 +98,9 @@ hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodePa
 hipError_t decode_blocks_per_cu(int dtype, int head_dim, int block_size, int* blocks);
 hipError_t launch_cache_write(int elem_bytes, const CacheWriteParams& p, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
+// (new token, query head) rows one multi-token workgroup covers
+int multi_token_rows_per_group();
+hipError_t launch_multi_token(int dtype, int head_dim, int block_size, MultiTokenParams p,
+                              hipStream_t stream);
 
 }  // namespace pa

@@ -1,0 +1,454 @@
+// multi_token.hip - the gfx950 kernel behind pa_multi_token: attention for several new
+// tokens per sequence over the paged cache (a prompt chunk, or draft tokens to verify).
+//
+// Pages cited (title, site): [ASP] "PagedAttention" awesome-system-papers, sections
+// 实现要点 (continuous batching adds sequences every step, so their prompt tokens are
+// attended through the same block tables) and 已知局限 (speculative decoding over the
+// paged cache); 引用本概念的论文 (the cache serves the scaled dot-product attention of
+// "Attention Is All You Need", where a token sees itself and every earlier token);
+// [RK] "什么是 LLM 中的分页注意力(Paged Attention)?它是如何工作的?" news.rkmt.cn, 块表.
+//
+// What is computed.  Sequence s has L tokens cached, the last n of them new; new token
+// j sits at position c + j (c = L - n) and attends to positions 0 .. c + j.  Rows of
+// the problem are (new token, query head) pairs; the G query heads of one KV head
+// share every K/V byte, so one KV head's rows form a dense (rows x tokens) problem,
+// which is where the matrix cores pay.
+//
+// Work.  A workgroup (4 waves) owns 128 consecutive rows of one (sequence, KV head):
+// row r is new token r / G, query head r % G of the group.  Each wave holds 32 rows as
+// two 16-row MFMA tiles.  The workgroup walks the sequence's tokens in 32-token chunks
+// up to the last position its rows may see; each chunk's K and V are gathered through
+// the block table once into LDS (double-buffered, the next chunk's loads in flight while
+// the current one is computed) and read there by all four waves.
+//
+// MFMA layouts (as in the decode kernel, rows of the problem on the N side):
+//   logits^T = K (32 tokens x D) . Q^T (D x 16 rows), two 16-token tiles per chunk
+//   taking tokens {8i..8i+3} and {8i+4..8i+7}, so lane (row c, quad i) ends up holding
+//   tokens 8i..8i+7 of row c: exactly the B operand (P^T) of
+//   O^T += V^T (16 dims x 32 tokens) . P^T (32 tokens x 16 rows).
+// K is stored in LDS in that MFMA row order ([tile][row][D], padded), V dimension-major
+// ([D][32 tokens], padded), so every operand is one 16-byte LDS read per lane.
+//
+// Masking.  Positions past the causal limit of a row are removed by select (-inf
+// before the max, weight 0).  Positions at or past L may hold anything, so they are
+// written to LDS as zeros and never multiplied.
+//
+// Launch.  One workgroup per (row tile, KV head, sequence), numbered so that the row
+// tiles of one (sequence, KV head) are dispatched to the same XCD (workgroups go to
+// the eight XCDs in turn), where they share that XCD's L2 copy of the K/V they all read.
+#include <math.h>
+
+#include <type_traits>
+
+#include "kernels.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVES = 4;
+constexpr int THREADS = WAVES * 64;
+constexpr int NTILE = 2;                    // 16-row MFMA tiles per wave
+constexpr int ROWS = WAVES * NTILE * 16;    // rows of one workgroup
+constexpr int CH = 32;                      // tokens per chunk
+constexpr int XCDS = 8;
+
+template <typename T>
+struct V8;
+template <>
+struct V8<__bf16> {
+  typedef bf16x8 type;
+};
+template <>
+struct V8<_Float16> {
+  typedef f16x8 type;
+};
+
+__device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, f32x4 v) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4*>(p) = v;
+  } else {
+    T t[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = (T)v[e];
+    *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, t);
+  }
+}
+
+template <typename T, int D, int BS>
+struct Shape {
+  static constexpr int E = sizeof(T);
+  static constexpr int EPL = 16 / E;                 // elements per 16 bytes
+  static constexpr int KL = D * E / 64;              // 16-byte operand reads per key row
+  static constexpr int NT = D / 16;                  // 16-dimension output tiles
+  static constexpr int KROW = D + EPL;               // LDS pitch of a key row (elements)
+  static constexpr int VROW = CH + EPL;              // LDS pitch of a value row
+  static constexpr int KSEG = D * E / 16;            // 16-byte pieces of a key row
+  static constexpr int KP = CH * KSEG / THREADS;     // key pieces per thread per chunk
+  static constexpr int VPE = EPL < BS ? EPL : BS;    // tokens per value piece
+  static constexpr int VSEG = CH / VPE;              // value pieces per dimension
+  static constexpr int VP = D * VSEG / THREADS;      // value pieces per thread per chunk
+  static_assert(KP >= 1 && VP >= 1, "chunk pieces must cover the workgroup");
+  typedef typename std::conditional<VPE * E == 16, u32x4, u32x2>::type VPiece;
+};
+
+// rows of the LDS key tile are in MFMA order: token t = 8a + 4q + b sits at 16q + 4a + b
+__device__ __forceinline__ int krow_of(int t) { return 16 * ((t >> 2) & 1) + 4 * (t >> 3) + (t & 3); }
+
+template <typename T, int D, int BS>
+__global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_kernel(MultiTokenParams P) {
+  typedef Shape<T, D, BS> SH;
+  constexpr int KL = SH::KL, NT = SH::NT, EPL = SH::EPL;
+  typedef typename SH::VPiece VPiece;
+
+  __shared__ __attribute__((aligned(16))) T sk[2][CH * SH::KROW];
+  __shared__ __attribute__((aligned(16))) T sv[2][D * SH::VROW];
+
+  // ---- which (row tile, KV head, sequence)
+  const int total = P.row_tiles * P.num_kv_heads * P.num_seqs;
+  const int logical = (int)(blockIdx.x % XCDS) * P.per_xcd + (int)(blockIdx.x / XCDS);
+  if (logical >= total) return;
+  const int x = logical % P.row_tiles;
+  const int rest = logical / P.row_tiles;
+  const int g = rest % P.num_kv_heads;
+  const int s = rest / P.num_kv_heads;
+
+  const int G = P.group, Hq = P.num_q_heads;
+  const int q0 = P.query_start[s], q1 = P.query_start[s + 1];
+  const int n = q1 - q0;
+  // rows that cannot be placed inside out[0 .. T) are never written
+  if (q0 < 0 || n < 0 || q1 > P.num_tokens) return;
+  const int nrows = n * G;
+  const int R0 = x * ROWS;
+  if (R0 >= nrows) return;
+  const int rend = min(nrows, R0 + ROWS);
+  const int L = P.seq_lens[s];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+
+  if (L > P.max_tokens || n > L) {  // a length the table cannot hold: NaN rows
+    for (int i = tid; i < (rend - R0) * D; i += THREADS) {
+      const int rr = R0 + i / D;
+      const int64_t row = (int64_t)(q0 + rr / G) * Hq + g * G + rr % G;
+      ((T*)P.out)[row * D + i % D] = (T)__builtin_nanf("");
+    }
+    return;
+  }
+  const int ctx = L - n;
+  const int lim_lo = ctx + R0 / G;          // the earliest causal limit among these rows
+  const int lim_hi = ctx + (rend - 1) / G;  // the latest
+  const int nch = lim_hi / CH + 1;
+  const int last_blk = (L - 1) / BS;
+
+  const uint32_t nblk32 = (uint32_t)min(P.num_blocks, (int64_t)0x7fffffff);
+  const int64_t tile = (int64_t)BS * D;
+  const int64_t blk_stride = (int64_t)P.num_kv_heads * tile;
+  const T* kbase = (const T*)P.k_cache + (int64_t)g * tile;
+  const T* vbase = (const T*)P.v_cache + (int64_t)g * tile;
+  const int32_t* tbl = P.block_tables + (int64_t)s * P.max_blocks;
+
+  // ---- this lane's rows: query fragments and causal limits
+  u32x4 qf[NTILE][KL];
+  int lim[NTILE];
+  bool rvalid[NTILE];
+  int64_t orow[NTILE];
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t) {
+    const int rr = R0 + wave * (NTILE * 16) + t * 16 + col;
+    rvalid[t] = rr < rend;
+    const int rc = min(rr, rend - 1);
+    const int j = rc / G;
+    lim[t] = ctx + j;
+    orow[t] = (int64_t)(q0 + j) * Hq + g * G + rc % G;
+    const T* qp = (const T*)P.q + orow[t] * D + quad * EPL;
+#pragma unroll
+    for (int c = 0; c < KL; ++c)
+      qf[t][c] = rvalid[t] ? *reinterpret_cast<const u32x4*>(qp + c * 4 * EPL) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // ---- chunk loading: block ids one chunk ahead of the data
+  int bad = 0;
+  int kid[SH::KP], vid[SH::VP];
+  u32x4 kr[SH::KP];
+  VPiece vr[SH::VP];
+  auto load_ids = [&](int c, int (&ki)[SH::KP], int (&vi)[SH::VP]) {
+    const int t0 = c * CH;
+#pragma unroll
+    for (int i = 0; i < SH::KP; ++i) {
+      const int t = (tid + THREADS * i) / SH::KSEG;
+      ki[i] = tbl[min((t0 + t) / BS, last_blk)];
+    }
+#pragma unroll
+    for (int i = 0; i < SH::VP; ++i) {
+      const int tk = ((tid + THREADS * i) % SH::VSEG) * SH::VPE;
+      vi[i] = tbl[min((t0 + tk) / BS, last_blk)];
+    }
+  };
+  auto load_data = [&](int c) {
+    const int t0 = c * CH;
+#pragma unroll
+    for (int i = 0; i < SH::KP; ++i) {
+      const int p = tid + THREADS * i;
+      const int pos = t0 + p / SH::KSEG;
+      const bool ok = (uint32_t)kid[i] < nblk32;
+      bad |= !ok;
+      const T* src = kbase + (int64_t)(ok ? kid[i] : 0) * blk_stride + (pos % BS) * D +
+                     (p % SH::KSEG) * EPL;
+      kr[i] = *reinterpret_cast<const u32x4*>(src);
+    }
+#pragma unroll
+    for (int i = 0; i < SH::VP; ++i) {
+      const int p = tid + THREADS * i;
+      const int d = p / SH::VSEG;
+      const int pos = t0 + (p % SH::VSEG) * SH::VPE;
+      const bool ok = (uint32_t)vid[i] < nblk32;
+      bad |= !ok;
+      const T* src = vbase + (int64_t)(ok ? vid[i] : 0) * blk_stride + d * BS + pos % BS;
+      vr[i] = *reinterpret_cast<const VPiece*>(src);
+    }
+  };
+  auto store_lds = [&](int c, int buf) {
+    const int t0 = c * CH;
+#pragma unroll
+    for (int i = 0; i < SH::KP; ++i) {
+      const int p = tid + THREADS * i;
+      const int t = p / SH::KSEG;
+      const u32x4 v = (t0 + t < L) ? kr[i] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&sk[buf][krow_of(t) * SH::KROW + (p % SH::KSEG) * EPL]) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < SH::VP; ++i) {
+      const int p = tid + THREADS * i;
+      const int d = p / SH::VSEG;
+      const int tk = (p % SH::VSEG) * SH::VPE;
+      VPiece v = vr[i];
+      if (t0 + tk + SH::VPE > L) {  // values at or past L may be NaN: zero them
+        constexpr int W = sizeof(VPiece) / 4;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          if constexpr (sizeof(T) == 2) {
+            const int e = t0 + tk + 2 * w;
+            v[w] &= (e < L ? 0x0000FFFFu : 0u) | (e + 1 < L ? 0xFFFF0000u : 0u);
+          } else {
+            v[w] = (t0 + tk + w < L) ? v[w] : 0u;
+          }
+        }
+      }
+      *reinterpret_cast<VPiece*>(&sv[buf][d * SH::VROW + tk]) = v;
+    }
+  };
+
+  float m_run[NTILE], l_run[NTILE];
+  f32x4 acc[NTILE][NT];
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn) acc[t][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto compute = [&](int c, int buf) {
+    const int t0 = c * CH;
+    // logits^T tiles a (tokens 8i..8i+3) and b (8i+4..8i+7); A read once for both row tiles
+    f32x4 sa[NTILE], sb[NTILE];
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) sa[t] = sb[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const T* ka = &sk[buf][col * SH::KROW + quad * EPL];
+    const T* kb = &sk[buf][(16 + col) * SH::KROW + quad * EPL];
+#pragma unroll
+    for (int k = 0; k < KL; ++k) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(ka + k * 4 * EPL);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(kb + k * 4 * EPL);
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) {
+        if constexpr (sizeof(T) == 2) {
+          typedef typename V8<T>::type VT;
+          sa[t] = mma16(__builtin_bit_cast(VT, a), __builtin_bit_cast(VT, qf[t][k]), sa[t]);
+          sb[t] = mma16(__builtin_bit_cast(VT, b), __builtin_bit_cast(VT, qf[t][k]), sb[t]);
+        } else {
+          const f32x4 af = __builtin_bit_cast(f32x4, a), bf = __builtin_bit_cast(f32x4, b);
+          const f32x4 qv = __builtin_bit_cast(f32x4, qf[t][k]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sa[t] = mma4(af[e], qv[e], sa[t]);
+            sb[t] = mma4(bf[e], qv[e], sb[t]);
+          }
+        }
+      }
+    }
+    // value operands: dimension 16nn + col, tokens 8quad .. 8quad+7
+    u32x4 vop[NT][SH::E / 2];
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn)
+#pragma unroll
+      for (int u = 0; u < SH::E / 2; ++u)
+        vop[nn][u] = *reinterpret_cast<const u32x4*>(&sv[buf][(16 * nn + col) * SH::VROW + 8 * quad + u * EPL]);
+
+    const bool masked = t0 + CH - 1 > lim_lo;  // uniform: a chunk crossing some row's limit
+    const int tfirst = t0 + 8 * quad;
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      float z[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z[e] = sa[t][e] * P.scale_log2;
+        z[4 + e] = sb[t][e] * P.scale_log2;
+      }
+      if (masked) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = (tfirst + e <= lim[t]) ? z[e] : -INFINITY;
+      }
+      float cm = z[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) cm = fmaxf(cm, z[e]);
+      cm = fmaxf(cm, __shfl_xor(cm, 16));
+      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      // every row sees position 0, so after the first chunk m_run is finite
+      const float m_new = fmaxf(m_run[t], cm);
+      const float alpha = exp2_fast(m_run[t] - m_new);
+      float pr[8], psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pr[e] = exp2_fast(z[e] - m_new);
+        psum += pr[e];
+      }
+      l_run[t] = l_run[t] * alpha + psum;
+      m_run[t] = m_new;
+#pragma unroll
+      for (int nn = 0; nn < NT; ++nn) acc[t][nn] *= alpha;
+      if constexpr (sizeof(T) == 2) {
+        // weights as hi + lo pairs of the input type (about fp32 accuracy)
+        typedef typename V8<T>::type VT;
+        VT phi, plo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const T h = (T)pr[e];
+          phi[e] = h;
+          plo[e] = (T)(pr[e] - (float)h);
+        }
+#pragma unroll
+        for (int nn = 0; nn < NT; ++nn) {
+          const VT vv = __builtin_bit_cast(VT, vop[nn][0]);
+          acc[t][nn] = mma16(vv, phi, acc[t][nn]);
+          acc[t][nn] = mma16(vv, plo, acc[t][nn]);
+        }
+      } else {
+#pragma unroll
+        for (int nn = 0; nn < NT; ++nn) {
+          const f32x4 lo = __builtin_bit_cast(f32x4, vop[nn][0]);
+          const f32x4 hi = __builtin_bit_cast(f32x4, vop[nn][1]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[t][nn] = mma4(lo[e], pr[e], acc[t][nn]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[t][nn] = mma4(hi[e], pr[4 + e], acc[t][nn]);
+        }
+      }
+    }
+  };
+
+  // ---- the chunk pipeline
+  load_ids(0, kid, vid);
+  load_data(0);
+  store_lds(0, 0);
+  if (nch > 1) load_ids(1, kid, vid);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) load_data(c + 1);
+    int kid2[SH::KP], vid2[SH::VP];
+    if (c + 2 < nch) load_ids(c + 2, kid2, vid2);
+    compute(c, buf);
+    if (c + 1 < nch) store_lds(c + 1, buf ^ 1);
+    if (c + 2 < nch) {
+#pragma unroll
+      for (int i = 0; i < SH::KP; ++i) kid[i] = kid2[i];
+#pragma unroll
+      for (int i = 0; i < SH::VP; ++i) vid[i] = vid2[i];
+    }
+    __syncthreads();
+  }
+  bad = __syncthreads_or(bad);
+
+  // ---- normalise and store
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t) {
+    float l = l_run[t];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!rvalid[t]) continue;
+    T* o = (T*)P.out + orow[t] * D + 4 * quad;
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn) {
+      f32x4 v = acc[t][nn] / l;
+      if (bad) v = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      store4(o + 16 * nn, v);
+    }
+  }
+}
+
+template <typename T, int D>
+const void* mt_bs(int bs) {
+  switch (bs) {
+    case 4: return (const void*)multi_token_kernel<T, D, 4>;
+    case 8: return (const void*)multi_token_kernel<T, D, 8>;
+    case 16: return (const void*)multi_token_kernel<T, D, 16>;
+    case 32: return (const void*)multi_token_kernel<T, D, 32>;
+  }
+  return nullptr;
+}
+
+template <typename T>
+const void* mt_d(int d, int bs) {
+  switch (d) {
+    case 64: return mt_bs<T, 64>(bs);
+    case 128: return mt_bs<T, 128>(bs);
+  }
+  return nullptr;
+}
+
+const void* multi_token_kernel_for(int dtype, int head_dim, int block_size) {
+  switch (dtype) {
+    case 0: return mt_d<float>(head_dim, block_size);
+    case 1: return mt_d<_Float16>(head_dim, block_size);
+    case 2: return mt_d<__bf16>(head_dim, block_size);
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+int multi_token_rows_per_group() { return ROWS; }
+
+hipError_t launch_multi_token(int dtype, int head_dim, int block_size, MultiTokenParams p,
+                              hipStream_t stream) {
+  const void* k = multi_token_kernel_for(dtype, head_dim, block_size);
+  const int64_t total = (int64_t)p.row_tiles * p.num_kv_heads * p.num_seqs;
+  if (!k || total <= 0 || total > 0x7fffffff - XCDS) return hipErrorInvalidValue;
+  p.per_xcd = (int32_t)((total + XCDS - 1) / XCDS);
+  void* args[] = {&p};
+  return hipLaunchKernel(k, dim3((unsigned)(p.per_xcd * XCDS)), dim3(THREADS), args, 0, stream);
+}
+
+}  // namespace pa

@@ -266,6 +266,68 @@ pa_status pa_cache_write(const void* k, const void* v, const int64_t* slot_mappi
   return PA_OK;
 }
 
+pa_status pa_multi_token(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens,
+                         const int32_t* query_start, int32_t block_size, int32_t num_kv_heads,
+                         float scale, void* out, const pa_multi_token_ext* ext) {
+  g_error.clear();
+  if (!ext) return fail(PA_ERR_INVALID_ARG, "ext is NULL");
+  const int32_t S = ext->num_seqs, T = ext->num_tokens, Hq = ext->num_q_heads, D = ext->head_dim;
+  const int32_t MB = ext->max_blocks_per_seq, bs = block_size, hkv = num_kv_heads;
+  if (S < 0 || S > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d outside [0, 65535]", S);
+  if (T < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %d < 0", T);
+  if (ext->max_query_len < 0) return fail(PA_ERR_INVALID_ARG, "max_query_len %d < 0", ext->max_query_len);
+  if (Hq <= 0) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d <= 0", Hq);
+  if (hkv <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d <= 0", hkv);
+  if (Hq % hkv) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", Hq, hkv);
+  if (D <= 0) return fail(PA_ERR_INVALID_ARG, "head_dim %d <= 0", D);
+  if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", D);
+  if (bs <= 0) return fail(PA_ERR_INVALID_ARG, "block_size %d <= 0", bs);
+  if (!block_size_built(bs)) return fail(PA_ERR_UNSUPPORTED, "block_size %d (built: 4, 8, 16, 32)", bs);
+  if (MB <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d <= 0", MB);
+  if (ext->num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks %lld <= 0", (long long)ext->num_blocks);
+  if (!dtype_valid(ext->dtype)) return fail(PA_ERR_INVALID_ARG, "dtype %d", ext->dtype);
+  const int64_t max_tokens = (int64_t)MB * bs;
+  if (max_tokens > (int64_t(1) << 30)) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size too large");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (S == 0 || T == 0 || ext->max_query_len == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start || !out)
+    return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return fail(PA_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(query_start, 4))
+    return fail(PA_ERR_INVALID_ARG, "block_tables, seq_lens and query_start must be 4-byte aligned");
+  const int32_t G = Hq / hkv;
+  const int64_t rows = (int64_t)std::min(ext->max_query_len, T) * G;
+  const int64_t tiles = (rows + pa::multi_token_rows_per_group() - 1) / pa::multi_token_rows_per_group();
+  if (tiles * hkv * S > (int64_t)INT32_MAX - 64)
+    return fail(PA_ERR_UNSUPPORTED, "%lld workgroups in one launch", (long long)(tiles * hkv * S));
+  if ((int64_t)T * G > (int64_t)INT32_MAX - 1024 || (int64_t)T * Hq * D > ((int64_t)1 << 40))
+    return fail(PA_ERR_UNSUPPORTED, "num_tokens %d too large for one launch", T);
+  pa::MultiTokenParams p;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.query_start = query_start;
+  p.out = out;
+  p.num_blocks = ext->num_blocks;
+  p.num_seqs = S;
+  p.num_tokens = T;
+  p.num_q_heads = Hq;
+  p.num_kv_heads = hkv;
+  p.group = G;
+  p.max_blocks = MB;
+  p.max_tokens = (int32_t)max_tokens;
+  p.row_tiles = (int32_t)tiles;
+  p.per_xcd = 0;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);  // log2(e)
+  const hipError_t e = pa::launch_multi_token(ext->dtype, D, bs, p, static_cast<hipStream_t>(ext->stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "multi-token launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
                          int32_t n, const pa_copy_blocks_ext* ext) {
   g_error.clear();

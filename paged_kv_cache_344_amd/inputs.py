@@ -64,6 +64,12 @@ CONFIGS = {
                            head_dim=128, block_size=32, max_blocks_per_seq=4096,
                            lens=("uniform", 32768, 131072), pool=("slack", 0.10),
                            cache_write=False, partition_size=512),
+    # chunked prefill: a 512-token prompt chunk per sequence on top of 1024-8192 cached
+    # tokens, GQA-8; every new token attends causally (pa_multi_token)
+    "prefill_bf16": dict(dtype="bf16", num_seqs=8, num_q_heads=64, num_kv_heads=8,
+                         head_dim=128, block_size=16, max_blocks_per_seq=544,
+                         lens=("chunk", 1024, 8192, 512), pool=("slack", 0.10),
+                         cache_write=False),
 }
 
 
@@ -82,9 +88,11 @@ class Batch:
     scale: float
     seq_lens: np.ndarray        # int32 [S]; counts every attended token, the new one included
     block_tables: np.ndarray    # int32 [S, max_blocks_per_seq], -1 past the used blocks
-    q: np.ndarray               # [S, Hq, D]
+    q: np.ndarray               # [S, Hq, D] ([T, Hq, D] for multi-token batches)
     k_cache: np.ndarray         # [N, Hkv, bs, D]
     v_cache: np.ndarray         # [N, Hkv, D, bs]
+    query_start: Optional[np.ndarray] = None  # int32 [S+1] for multi-token batches: q rows
+                                              # of sequence s are qs[s] .. qs[s+1]-1
     k_new: Optional[np.ndarray] = None      # [T, Hkv, D]
     v_new: Optional[np.ndarray] = None      # [T, Hkv, D]
     slot_mapping: Optional[np.ndarray] = None  # int64 [T]
@@ -158,6 +166,9 @@ def _draw_lengths(rng, spec, S):
         lo, hi = spec[1], spec[2]
         u = rng.uniform(math.log(lo), math.log(hi + 1), size=S)
         return np.clip(np.floor(np.exp(u)).astype(np.int64), lo, hi), None
+    if kind == "chunk":  # cached context uniform in [lo, hi], then n new tokens
+        lo, hi, n = spec[1], spec[2], spec[3]
+        return rng.integers(lo, hi + 1, size=S) + n, None
     if kind == "prefix":
         prefix, lo, hi = spec[1], spec[2], spec[3]
         private = rng.integers(lo, hi + 1, size=S)
@@ -167,7 +178,8 @@ def _draw_lengths(rng, spec, S):
 
 def make_batch(name: str, seed: int = 0, **over) -> Batch:
     """Build one seeded batch.  ``over`` replaces recipe fields (e.g. ``num_seqs``,
-    ``lens``, ``dtype``, ``q_gain`` to multiply Q for a peaked softmax)."""
+    ``lens``, ``dtype``, ``q_gain`` to multiply Q for a peaked softmax, ``new_tokens``
+    to give each sequence that many query tokens, its last ones, for pa_multi_token)."""
     cfg = dict(CONFIGS[name])
     q_gain = over.pop("q_gain", 1.0)
     cfg.update(over)
@@ -208,7 +220,17 @@ def make_batch(name: str, seed: int = 0, **over) -> Batch:
         nxt += n_own
         bt[s, :len(row)] = row
 
-    q32 = rng.standard_normal((S, Hq, D), dtype=np.float32)
+    qs = None
+    if cfg["lens"][0] == "chunk" or "new_tokens" in cfg:
+        # the last n_s cached tokens of each sequence are new and each has a query
+        if "new_tokens" in cfg:
+            new = np.minimum(np.asarray(cfg["new_tokens"], dtype=np.int64), lens)
+        else:
+            new = np.full(S, cfg["lens"][3], dtype=np.int64)
+        qs = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+        q32 = rng.standard_normal((int(qs[-1]), Hq, D), dtype=np.float32)
+    else:
+        q32 = rng.standard_normal((S, Hq, D), dtype=np.float32)
     if q_gain != 1.0:
         q32 *= np.float32(q_gain)
 
@@ -245,7 +267,7 @@ def make_batch(name: str, seed: int = 0, **over) -> Batch:
     return Batch(name=name, seed=seed, dtype=dtype, num_seqs=S, num_q_heads=Hq,
                  num_kv_heads=Hkv, head_dim=D, block_size=bs, max_blocks_per_seq=MB,
                  num_blocks=N, scale=scale, seq_lens=lens.astype(np.int32), block_tables=bt,
-                 q=to_storage(q32, dtype), k_cache=k_cache, v_cache=v_cache,
+                 q=to_storage(q32, dtype), k_cache=k_cache, v_cache=v_cache, query_start=qs,
                  k_new=k_new, v_new=v_new,
                  slot_mapping=None if slots is None else slots.astype(np.int64),
                  partition_size=int(cfg.get("partition_size", 0)), shared_blocks=shared)

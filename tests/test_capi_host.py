@@ -199,3 +199,43 @@ def test_copy_blocks_pointer_checks(lib):
     assert lib.pa_copy_blocks(FAKE, FAKE, None, None, 1, ctypes.byref(e)) == B.PA_ERR_INVALID_ARG
     assert lib.pa_copy_blocks(FAKE, FAKE, None, None, -1, ctypes.byref(e)) == B.PA_ERR_INVALID_ARG
     assert _cb(lib, [], [], ptr=0) == B.PA_OK     # nothing to copy
+
+
+def _mt(lib, ptr=FAKE, ext=True, scale=0.1, bs=16, hkv=8, **kw):
+    base = dict(num_seqs=4, num_tokens=64, max_query_len=32, num_q_heads=64, head_dim=128,
+                max_blocks_per_seq=64, num_blocks=100, dtype=B.PA_BF16, stream=None)
+    base.update(kw)
+    e = B.MultiTokenExt(**base)
+    return lib.pa_multi_token(ptr, ptr, ptr, ptr, ptr, ptr, bs, hkv, ctypes.c_float(scale), ptr,
+                              ctypes.byref(e) if ext else None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(num_seqs=-1), B.PA_ERR_INVALID_ARG),
+    (dict(num_seqs=70000), B.PA_ERR_INVALID_ARG),
+    (dict(num_tokens=-1), B.PA_ERR_INVALID_ARG),
+    (dict(max_query_len=-1), B.PA_ERR_INVALID_ARG),
+    (dict(num_q_heads=60), B.PA_ERR_INVALID_ARG),         # not a multiple of Hkv
+    (dict(head_dim=96), B.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=0), B.PA_ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=0), B.PA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), B.PA_ERR_INVALID_ARG),
+    (dict(dtype=9), B.PA_ERR_INVALID_ARG),
+    (dict(bs=12), B.PA_ERR_UNSUPPORTED),
+    (dict(bs=0), B.PA_ERR_INVALID_ARG),
+    (dict(hkv=0), B.PA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), B.PA_ERR_INVALID_ARG),
+    (dict(ptr=0), B.PA_ERR_INVALID_ARG),
+    (dict(ptr=FAKE + 4), B.PA_ERR_INVALID_ARG),
+    (dict(ext=False), B.PA_ERR_INVALID_ARG),
+    (dict(num_tokens=1 << 30, max_query_len=1 << 30), B.PA_ERR_UNSUPPORTED),
+])
+def test_multi_token_rejects(lib, kw, want):
+    assert _mt(lib, **kw) == want
+    assert lib.pa_last_error()
+
+
+def test_multi_token_nothing_to_do(lib):
+    assert _mt(lib, ptr=0, num_seqs=0) == B.PA_OK
+    assert _mt(lib, ptr=0, num_tokens=0) == B.PA_OK
+    assert _mt(lib, ptr=0, max_query_len=0) == B.PA_OK
