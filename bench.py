@@ -16,7 +16,8 @@ Reported (one JSON line on stdout):
              against 8 TB/s
   cpu_baseline  the fp64 oracle on the host cores, on the same batch
   parity     GPU output of the last timed step against the oracle
-  also       the same decode-only measurement for the long-context batches
+  also       the same decode-only measurement for the long-context batches, and the
+             chunked-prefill batch through pa_multi_token (flops against the MFMA peak)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -34,6 +35,7 @@ if ROOT not in sys.path:
 
 METRIC = "attended KV tokens/s and achieved HBM GB/s (% of peak), decode, 1 MI355X"
 PEAK_GBPS = 8000.0  # MI355X HBM3E peak
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # dense MFMA (f32: vector peak)
 MALL_BYTES = 256 << 20
 CALIBRATION_BYTES = 256 << 20
 HEADLINE = "gqa_bf16"
@@ -51,6 +53,9 @@ WORKLOAD_TEXT = {
                 "lengths uniform in [128, 2048]",
     "prefix_bf16": "bf16 prefix-sharing decode: 64 seqs sharing a 1024-token prefix, "
                    "0-512 private tokens, 32 q / 8 KV heads, head_dim 128, block_size 16",
+    "prefill_bf16": "bf16 chunked prefill (pa_multi_token): 8 seqs, a 512-token chunk each on "
+                    "1024-8192 cached tokens, causal, 64 q / 8 KV heads, head_dim 128, "
+                    "block_size 16",
 }
 
 
@@ -77,6 +82,29 @@ def decode_bytes(b, unique_shared=True):
     return tokens * row + 2 * b.num_seqs * b.num_q_heads * b.head_dim * e + 4 * nb + 4 * b.num_seqs
 
 
+def multi_token_flops(b):
+    """Algorithmic flops of one pa_multi_token call: for every (new token, query head)
+    pair and every position it sees, a D-long dot product and a D-long weighted sum
+    (4D flops)."""
+    import numpy as np
+    qs = b.query_start.astype(np.int64)
+    n = np.diff(qs)
+    ctx = b.seq_lens.astype(np.int64) - n
+    seen = int((n * ctx + n * (n + 1) // 2).sum())  # sum over j < n of (ctx + j + 1)
+    return seen * b.num_q_heads * 4 * b.head_dim
+
+
+def multi_token_bytes(b):
+    """Algorithmic HBM bytes of one pa_multi_token call: each sequence's K and V read
+    once, queries read and outputs written once, tables and lengths read."""
+    import numpy as np
+    e = elem_bytes(b.dtype)
+    T = int(b.query_start[-1])
+    nb = int(((b.seq_lens.astype(np.int64) + b.block_size - 1) // b.block_size).sum())
+    return (b.total_tokens() * b.num_kv_heads * b.head_dim * e * 2 + 2 * T * b.num_q_heads *
+            b.head_dim * e + 4 * nb + 8 * b.num_seqs + 4)
+
+
 def cache_write_bytes(b):
     if b.slot_mapping is None:
         return 0
@@ -97,10 +125,17 @@ class Copy:
         self.bt = torch.from_numpy(b.block_tables).to(dev)
         self.sl = torch.from_numpy(b.seq_lens).to(dev)
         self.out = torch.empty_like(self.q)
+        self.write = None
+        if b.query_start is not None:  # a multi-token batch: pa_multi_token in place of decode
+            self.qs = torch.from_numpy(b.query_start).to(dev)
+            self.decode = pa.PreparedMultiToken(
+                self.q, self.kc, self.vc, self.bt, self.sl, self.qs, b.block_size,
+                b.num_kv_heads, b.scale, self.out,
+                max_query_len=int((b.query_start[1:] - b.query_start[:-1]).max()))
+            return
         self.decode = pa.PreparedDecode(self.q, self.kc, self.vc, self.bt, self.sl, b.block_size,
                                         b.num_kv_heads, b.scale, self.out,
                                         partition_size=partition_size)
-        self.write = None
         if b.slot_mapping is not None:
             self.kn, self.vn = t(b.k_new), t(b.v_new)
             self.sm = torch.from_numpy(b.slot_mapping).to(dev)
@@ -220,6 +255,8 @@ def measure(name, seed, steps, warmup, copies_min, with_write):
     dec_bytes = decode_bytes(b)
     mean_ms = sum(dms) / len(dms)
     srt = sorted(dms)
+    if b.query_start is not None:
+        dec_bytes = multi_token_bytes(b)
     res = dict(batch=b, copies=copies, elapsed=elapsed, decode_ms=mean_ms,
                decode_ms_p10=srt[len(srt) // 10], decode_ms_p90=srt[(9 * len(srt)) // 10],
                decode_bytes=dec_bytes, write_bytes=cache_write_bytes(b) if with_write else 0,
@@ -239,7 +276,7 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="minimum rotated copies of a batch")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--also", default="long_bf16_bs16,long_bf16_bs32",
+    ap.add_argument("--also", default="long_bf16_bs16,long_bf16_bs32,prefill_bf16",
                     help="comma-separated secondary batches measured decode-only ('' for none)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 256 MiB device-to-device copy, a dispatch of known size "
@@ -289,6 +326,21 @@ def main():
     for name in [x for x in args.also.split(",") if x]:
         r = measure(name, args.seed, max(20, args.steps // 4), args.warmup, 1, with_write=False)
         rb = r["batch"]
+        if rb.query_start is not None:
+            fl = multi_token_flops(rb)
+            tf = fl / (r["decode_ms"] * 1e-3) / 1e12
+            also[name] = dict(workload=WORKLOAD_TEXT.get(name, name),
+                              new_tokens=int(rb.query_start[-1]), sum_L=rb.total_tokens(),
+                              call_us=r["decode_ms"] * 1e3, call_us_p10=r["decode_ms_p10"] * 1e3,
+                              call_us_p90=r["decode_ms_p90"] * 1e3, algorithmic_flops=fl,
+                              roofline={"bound": "mfma", "achieved": tf,
+                                        "peak": PEAK_TFLOPS[rb.dtype], "unit": "TFLOP/s",
+                                        "frac": tf / PEAK_TFLOPS[rb.dtype]},
+                              algorithmic_bytes=r["decode_bytes"], achieved_gbps=r["gbps"])
+            log(f"{name}: {tf:.0f} TFLOP/s = {tf / PEAK_TFLOPS[rb.dtype]:.1%} of dense MFMA peak")
+            del r
+            torch.cuda.empty_cache()
+            continue
         also[name] = dict(workload=WORKLOAD_TEXT.get(name, name), sum_L=rb.total_tokens(),
                           tokens_per_s=rb.total_tokens() / (r["decode_ms"] * 1e-3),
                           decode_us=r["decode_ms"] * 1e3, decode_us_p10=r["decode_ms_p10"] * 1e3,

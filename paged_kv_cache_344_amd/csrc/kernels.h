@@ -75,7 +75,6 @@ struct MultiTokenParams {
   int32_t max_blocks;           // row stride of block_tables
   int32_t max_tokens;           // max_blocks * bs
   int32_t row_tiles;            // workgroup row tiles per (sequence, KV head)
-  int32_t per_xcd;              // set by the launcher
   float scale_log2;             // scale * log2(e)
 };
 

@@ -33,9 +33,15 @@
 // before the max, weight 0).  Positions at or past L may hold anything, so they are
 // written to LDS as zeros and never multiplied.
 //
-// Launch.  One workgroup per (row tile, KV head, sequence), numbered so that the row
-// tiles of one (sequence, KV head) are dispatched to the same XCD (workgroups go to
-// the eight XCDs in turn), where they share that XCD's L2 copy of the K/V they all read.
+// Precision.  Products accumulate in fp32.  The softmax weights enter the second product
+// as a hi + lo pair for bf16 (its 8 significant bits alone would show next to the
+// output's own rounding), rounded once for fp16, and exactly for fp32; the sum that
+// normalises them is kept in fp32.
+//
+// Launch.  One workgroup per (row tile, KV head, sequence).  Workgroups are dispatched
+// to the eight XCDs in turn; the numbering deals whole (sequence, KV head) groups to
+// the XCDs round-robin, so that the row tiles of a group share their XCD's L2 copy of
+// the K/V they all read, and every XCD gets a share of every sequence.
 #include <math.h>
 
 #include <type_traits>
@@ -121,14 +127,15 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
   __shared__ __attribute__((aligned(16))) T sk[2][CH * SH::KROW];
   __shared__ __attribute__((aligned(16))) T sv[2][D * SH::VROW];
 
-  // ---- which (row tile, KV head, sequence)
-  const int total = P.row_tiles * P.num_kv_heads * P.num_seqs;
-  const int logical = (int)(blockIdx.x % XCDS) * P.per_xcd + (int)(blockIdx.x / XCDS);
-  if (logical >= total) return;
-  const int x = logical % P.row_tiles;
-  const int rest = logical / P.row_tiles;
-  const int g = rest % P.num_kv_heads;
-  const int s = rest / P.num_kv_heads;
+  // ---- which (row tile, KV head, sequence): (sequence, KV head) groups are dealt to
+  // the XCDs in turn, and every row tile of a group runs on its group's XCD
+  const int xcd = (int)(blockIdx.x % XCDS);
+  const int idx = (int)(blockIdx.x / XCDS);
+  const int group = (idx / P.row_tiles) * XCDS + xcd;
+  if (group >= P.num_kv_heads * P.num_seqs) return;
+  const int x = idx % P.row_tiles;
+  const int g = group % P.num_kv_heads;
+  const int s = group / P.num_kv_heads;
 
   const int G = P.group, Hq = P.num_q_heads;
   const int q0 = P.query_start[s], q1 = P.query_start[s + 1];
@@ -336,10 +343,16 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
       }
       l_run[t] = l_run[t] * alpha + psum;
       m_run[t] = m_new;
+      // after the first chunks the running maximum rarely moves: rescale only when it
+      // moved for some row of this wave
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int nn = 0; nn < NT; ++nn) acc[t][nn] *= alpha;
-      if constexpr (sizeof(T) == 2) {
-        // weights as hi + lo pairs of the input type (about fp32 accuracy)
+        for (int nn = 0; nn < NT; ++nn) acc[t][nn] *= alpha;
+      }
+      if constexpr (std::is_same<T, __bf16>::value) {
+        // bf16 keeps 8 significant bits: the weights go in as a hi + lo pair (two
+        // MFMAs), about fp32 accuracy, so that the output's own rounding is the only
+        // visible error
         typedef typename V8<T>::type VT;
         VT phi, plo;
 #pragma unroll
@@ -354,6 +367,16 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
           acc[t][nn] = mma16(vv, phi, acc[t][nn]);
           acc[t][nn] = mma16(vv, plo, acc[t][nn]);
         }
+      } else if constexpr (sizeof(T) == 2) {
+        // fp16 keeps 11 significant bits: one rounding of each weight is far inside
+        // the tolerance; the sum that normalises them stays fp32
+        typedef typename V8<T>::type VT;
+        VT ph;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ph[e] = (T)pr[e];
+#pragma unroll
+        for (int nn = 0; nn < NT; ++nn)
+          acc[t][nn] = mma16(__builtin_bit_cast(VT, vop[nn][0]), ph, acc[t][nn]);
       } else {
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn) {
@@ -444,11 +467,11 @@ int multi_token_rows_per_group() { return ROWS; }
 hipError_t launch_multi_token(int dtype, int head_dim, int block_size, MultiTokenParams p,
                               hipStream_t stream) {
   const void* k = multi_token_kernel_for(dtype, head_dim, block_size);
-  const int64_t total = (int64_t)p.row_tiles * p.num_kv_heads * p.num_seqs;
-  if (!k || total <= 0 || total > 0x7fffffff - XCDS) return hipErrorInvalidValue;
-  p.per_xcd = (int32_t)((total + XCDS - 1) / XCDS);
+  const int64_t groups = (int64_t)p.num_kv_heads * p.num_seqs;
+  const int64_t per_xcd = (groups + XCDS - 1) / XCDS * p.row_tiles;
+  if (!k || groups <= 0 || p.row_tiles <= 0 || per_xcd * XCDS > 0x7fffffff) return hipErrorInvalidValue;
   void* args[] = {&p};
-  return hipLaunchKernel(k, dim3((unsigned)(p.per_xcd * XCDS)), dim3(THREADS), args, 0, stream);
+  return hipLaunchKernel(k, dim3((unsigned)(per_xcd * XCDS)), dim3(THREADS), args, 0, stream);
 }
 
 }  // namespace pa

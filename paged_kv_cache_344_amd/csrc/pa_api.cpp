@@ -300,8 +300,8 @@ pa_status pa_multi_token(const void* q, const void* k_cache, const void* v_cache
   const int32_t G = Hq / hkv;
   const int64_t rows = (int64_t)std::min(ext->max_query_len, T) * G;
   const int64_t tiles = (rows + pa::multi_token_rows_per_group() - 1) / pa::multi_token_rows_per_group();
-  if (tiles * hkv * S > (int64_t)INT32_MAX - 64)
-    return fail(PA_ERR_UNSUPPORTED, "%lld workgroups in one launch", (long long)(tiles * hkv * S));
+  const int64_t wgs = ((int64_t)S * hkv + 7) / 8 * 8 * tiles;  // groups dealt to 8 XCDs
+  if (wgs > (int64_t)INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "%lld workgroups in one launch", (long long)wgs);
   if ((int64_t)T * G > (int64_t)INT32_MAX - 1024 || (int64_t)T * Hq * D > ((int64_t)1 << 40))
     return fail(PA_ERR_UNSUPPORTED, "num_tokens %d too large for one launch", T);
   pa::MultiTokenParams p;
@@ -321,7 +321,6 @@ pa_status pa_multi_token(const void* q, const void* k_cache, const void* v_cache
   p.max_blocks = MB;
   p.max_tokens = (int32_t)max_tokens;
   p.row_tiles = (int32_t)tiles;
-  p.per_xcd = 0;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);  // log2(e)
   const hipError_t e = pa::launch_multi_token(ext->dtype, D, bs, p, static_cast<hipStream_t>(ext->stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "multi-token launch: %s", hipGetErrorString(e));
