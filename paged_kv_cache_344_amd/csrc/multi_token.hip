@@ -57,6 +57,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+#define AS4 __attribute__((address_space(4)))  // constant address space: scalar loads
+
 constexpr int WAVES = 4;
 constexpr int THREADS = WAVES * 64;
 constexpr int NTILE = 2;                    // 16-row MFMA tiles per wave
@@ -85,6 +87,21 @@ __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Lanes c, c + 16, c + 32 and c + 48 (the four quads) hold parts of the same row: reduce
+// over them with the gfx950 lane-swap instructions (VALU, no LDS round trip).
+__device__ __forceinline__ float max_over_quads(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));  // lanes l and l ^ 32
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));  // and l ^ 16
+}
+__device__ __forceinline__ float sum_over_quads(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, f32x4 v) {
@@ -194,45 +211,55 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
       qf[t][c] = rvalid[t] ? *reinterpret_cast<const u32x4*>(qp + c * 4 * EPL) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // ---- chunk loading: block ids one chunk ahead of the data
+  // ---- chunk loading, block ids one chunk ahead of the data.  Key piece p (of a
+  // thread's KP) is token p / KSEG of the chunk, 16-byte segment p % KSEG of its row;
+  // value piece p is dimension p % D, tokens VPE * (p / D) onwards.  One wave-wide load
+  // instruction thus covers whole token groups, and the physical block it reads is the
+  // same for all its lanes: one scalar table read per instruction, and the block's
+  // address is formed in scalar registers.  Only 8-token key groups at block size 4
+  // span two blocks; there each lane picks one of the two.
+  constexpr int TPI = 64 / SH::KSEG;              // tokens under one wave-wide key load
+  constexpr int NBK = TPI > BS ? TPI / BS : 1;    // blocks those tokens span
+  static_assert(NBK <= 2, "a key load spans at most two blocks");
+  const int32_t AS4* tbls = (const int32_t AS4*)tbl;
   int bad = 0;
-  int kid[SH::KP], vid[SH::VP];
+  int kid[SH::KP][NBK], vid[SH::VP];
   u32x4 kr[SH::KP];
   VPiece vr[SH::VP];
-  auto load_ids = [&](int c, int (&ki)[SH::KP], int (&vi)[SH::VP]) {
-    const int t0 = c * CH;
-#pragma unroll
-    for (int i = 0; i < SH::KP; ++i) {
-      const int t = (tid + THREADS * i) / SH::KSEG;
-      ki[i] = tbl[min((t0 + t) / BS, last_blk)];
-    }
-#pragma unroll
-    for (int i = 0; i < SH::VP; ++i) {
-      const int tk = ((tid + THREADS * i) % SH::VSEG) * SH::VPE;
-      vi[i] = tbl[min((t0 + tk) / BS, last_blk)];
-    }
+  auto block_id = [&](int j) {  // wave-uniform table read; ids outside the pool -> 0
+    const int id = tbls[min(j, last_blk)];
+    const bool ok = (uint32_t)id < nblk32;
+    bad |= !ok;
+    return ok ? id : 0;
   };
-  auto load_data = [&](int c) {
+  auto load_ids = [&](int c, int (&ki)[SH::KP][NBK], int (&vi)[SH::VP]) {
     const int t0 = c * CH;
 #pragma unroll
     for (int i = 0; i < SH::KP; ++i) {
+      const int j = (t0 + (64 * wave + THREADS * i) / SH::KSEG) / BS;
+#pragma unroll
+      for (int u = 0; u < NBK; ++u) ki[i][u] = block_id(j + u);
+    }
+#pragma unroll
+    for (int i = 0; i < SH::VP; ++i)
+      vi[i] = block_id((t0 + ((64 * wave + THREADS * i) / D) * SH::VPE) / BS);
+  };
+  auto load_data = [&]() {
+#pragma unroll
+    for (int i = 0; i < SH::KP; ++i) {
       const int p = tid + THREADS * i;
-      const int pos = t0 + p / SH::KSEG;
-      const bool ok = (uint32_t)kid[i] < nblk32;
-      bad |= !ok;
-      const T* src = kbase + (int64_t)(ok ? kid[i] : 0) * blk_stride + (pos % BS) * D +
-                     (p % SH::KSEG) * EPL;
-      kr[i] = *reinterpret_cast<const u32x4*>(src);
+      const int t = p / SH::KSEG;  // (t0 + t) % BS == t % BS: chunks start on block edges
+      int id = kid[i][0];
+      if constexpr (NBK == 2) id = ((t % TPI) >= BS) ? kid[i][1] : kid[i][0];
+      const T* blk = kbase + (int64_t)id * blk_stride;
+      kr[i] = *reinterpret_cast<const u32x4*>(blk + (t % BS) * D + (p % SH::KSEG) * EPL);
     }
 #pragma unroll
     for (int i = 0; i < SH::VP; ++i) {
       const int p = tid + THREADS * i;
-      const int d = p / SH::VSEG;
-      const int pos = t0 + (p % SH::VSEG) * SH::VPE;
-      const bool ok = (uint32_t)vid[i] < nblk32;
-      bad |= !ok;
-      const T* src = vbase + (int64_t)(ok ? vid[i] : 0) * blk_stride + d * BS + pos % BS;
-      vr[i] = *reinterpret_cast<const VPiece*>(src);
+      const int tk = (p / D) * SH::VPE;
+      const T* blk = vbase + (int64_t)vid[i] * blk_stride;
+      vr[i] = *reinterpret_cast<const VPiece*>(blk + (p % D) * BS + tk % BS);
     }
   };
   auto store_lds = [&](int c, int buf) {
@@ -247,8 +274,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
 #pragma unroll
     for (int i = 0; i < SH::VP; ++i) {
       const int p = tid + THREADS * i;
-      const int d = p / SH::VSEG;
-      const int tk = (p % SH::VSEG) * SH::VPE;
+      const int tk = (p / D) * SH::VPE;
       VPiece v = vr[i];
       if (t0 + tk + SH::VPE > L) {  // values at or past L may be NaN: zero them
         constexpr int W = sizeof(VPiece) / 4;
@@ -262,7 +288,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
           }
         }
       }
-      *reinterpret_cast<VPiece*>(&sv[buf][d * SH::VROW + tk]) = v;
+      *reinterpret_cast<VPiece*>(&sv[buf][(p % D) * SH::VROW + tk]) = v;
     }
   };
 
@@ -276,8 +302,12 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
     for (int nn = 0; nn < NT; ++nn) acc[t][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // One chunk: logits for both row tiles (the key operand read once for both), then per
+  // tile the softmax and the weighted sum.  Only a chunk that crosses the causal limit of
+  // some row of the workgroup is masked.
   auto compute = [&](int c, int buf) {
     const int t0 = c * CH;
+    const bool masked = t0 + CH - 1 > lim_lo;  // uniform
     // logits^T tiles a (tokens 8i..8i+3) and b (8i+4..8i+7); A read once for both row tiles
     f32x4 sa[NTILE], sb[NTILE];
 #pragma unroll
@@ -305,16 +335,9 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
         }
       }
     }
-    // value operands: dimension 16nn + col, tokens 8quad .. 8quad+7
-    u32x4 vop[NT][SH::E / 2];
-#pragma unroll
-    for (int nn = 0; nn < NT; ++nn)
-#pragma unroll
-      for (int u = 0; u < SH::E / 2; ++u)
-        vop[nn][u] = *reinterpret_cast<const u32x4*>(&sv[buf][(16 * nn + col) * SH::VROW + 8 * quad + u * EPL]);
-
-    const bool masked = t0 + CH - 1 > lim_lo;  // uniform: a chunk crossing some row's limit
+    // per row tile: softmax of the chunk, then its weighted sum
     const int tfirst = t0 + 8 * quad;
+    const T* vrow = &sv[buf][col * SH::VROW + 8 * quad];  // dimension 16nn + col, tokens 8quad..
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
       float z[8];
@@ -327,11 +350,9 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
 #pragma unroll
         for (int e = 0; e < 8; ++e) z[e] = (tfirst + e <= lim[t]) ? z[e] : -INFINITY;
       }
-      float cm = z[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) cm = fmaxf(cm, z[e]);
-      cm = fmaxf(cm, __shfl_xor(cm, 16));
-      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      float cm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                       fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+      cm = max_over_quads(cm);
       // every row sees position 0, so after the first chunk m_run is finite
       const float m_new = fmaxf(m_run[t], cm);
       const float alpha = exp2_fast(m_run[t] - m_new);
@@ -349,39 +370,29 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn) acc[t][nn] *= alpha;
       }
-      if constexpr (std::is_same<T, __bf16>::value) {
-        // bf16 keeps 8 significant bits: the weights go in as a hi + lo pair (two
-        // MFMAs), about fp32 accuracy, so that the output's own rounding is the only
-        // visible error
+      if constexpr (sizeof(T) == 2) {
         typedef typename V8<T>::type VT;
         VT phi, plo;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const T h = (T)pr[e];
           phi[e] = h;
-          plo[e] = (T)(pr[e] - (float)h);
+          // bf16 keeps 8 significant bits: the weights go in as a hi + lo pair (two
+          // MFMAs), about fp32 accuracy, so that the output's own rounding is the
+          // only visible error; fp16's 11 bits need one rounding only
+          if constexpr (std::is_same<T, __bf16>::value) plo[e] = (T)(pr[e] - (float)h);
         }
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn) {
-          const VT vv = __builtin_bit_cast(VT, vop[nn][0]);
+          const VT vv = *reinterpret_cast<const VT*>(vrow + 16 * nn * SH::VROW);
           acc[t][nn] = mma16(vv, phi, acc[t][nn]);
-          acc[t][nn] = mma16(vv, plo, acc[t][nn]);
+          if constexpr (std::is_same<T, __bf16>::value) acc[t][nn] = mma16(vv, plo, acc[t][nn]);
         }
-      } else if constexpr (sizeof(T) == 2) {
-        // fp16 keeps 11 significant bits: one rounding of each weight is far inside
-        // the tolerance; the sum that normalises them stays fp32
-        typedef typename V8<T>::type VT;
-        VT ph;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ph[e] = (T)pr[e];
-#pragma unroll
-        for (int nn = 0; nn < NT; ++nn)
-          acc[t][nn] = mma16(__builtin_bit_cast(VT, vop[nn][0]), ph, acc[t][nn]);
       } else {
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn) {
-          const f32x4 lo = __builtin_bit_cast(f32x4, vop[nn][0]);
-          const f32x4 hi = __builtin_bit_cast(f32x4, vop[nn][1]);
+          const f32x4 lo = *reinterpret_cast<const f32x4*>(vrow + 16 * nn * SH::VROW);
+          const f32x4 hi = *reinterpret_cast<const f32x4*>(vrow + 16 * nn * SH::VROW + 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[t][nn] = mma4(lo[e], pr[e], acc[t][nn]);
 #pragma unroll
@@ -393,20 +404,22 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
 
   // ---- the chunk pipeline
   load_ids(0, kid, vid);
-  load_data(0);
+  load_data();
   store_lds(0, 0);
   if (nch > 1) load_ids(1, kid, vid);
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
     const int buf = c & 1;
-    if (c + 1 < nch) load_data(c + 1);
-    int kid2[SH::KP], vid2[SH::VP];
+    if (c + 1 < nch) load_data();
+    int kid2[SH::KP][NBK], vid2[SH::VP];
     if (c + 2 < nch) load_ids(c + 2, kid2, vid2);
     compute(c, buf);
     if (c + 1 < nch) store_lds(c + 1, buf ^ 1);
     if (c + 2 < nch) {
 #pragma unroll
-      for (int i = 0; i < SH::KP; ++i) kid[i] = kid2[i];
+      for (int i = 0; i < SH::KP; ++i)
+#pragma unroll
+        for (int u = 0; u < NBK; ++u) kid[i][u] = kid2[i][u];
 #pragma unroll
       for (int i = 0; i < SH::VP; ++i) vid[i] = vid2[i];
     }
@@ -417,9 +430,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
   // ---- normalise and store
 #pragma unroll
   for (int t = 0; t < NTILE; ++t) {
-    float l = l_run[t];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = sum_over_quads(l_run[t]);
     if (!rvalid[t]) continue;
     T* o = (T*)P.out + orow[t] * D + 4 * quad;
 #pragma unroll
