@@ -90,17 +90,54 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 // Lanes c, c + 16, c + 32 and c + 48 (the four quads) hold parts of the same row: reduce
 // over them with the gfx950 lane-swap instructions (VALU, no LDS round trip).
+__device__ __forceinline__ float vmax(float a, float b) {  // v_max_f32, no canonicalisation
+  float m;
+  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(a), "v"(b));
+  return m;
+}
 __device__ __forceinline__ float max_over_quads(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));  // lanes l and l ^ 32
+  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));  // lanes l and l ^ 32
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));  // and l ^ 16
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));  // and l ^ 16
 }
 __device__ __forceinline__ float sum_over_quads(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// maximum of eight values as three v_max3 and one v_max (no NaN canonicalisation steps)
+__device__ __forceinline__ float max8(const float (&z)[8]) {
+  float a, b, c, m;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(a) : "v"(z[0]), "v"(z[1]), "v"(z[2]));
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(b) : "v"(z[3]), "v"(z[4]), "v"(z[5]));
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(c) : "v"(a), "v"(b), "v"(z[6]));
+  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(c), "v"(z[7]));
+  return m;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// eight weights as MFMA operands of a 16-bit type: hi = nearest T, and (bf16 only)
+// lo = nearest T to the remainder, converted two at a time
+template <typename T>
+__device__ __forceinline__ void split_weights(const float (&p)[8], u32x4& hi, u32x4& lo) {
+  typedef typename std::conditional<std::is_same<T, __bf16>::value, bf16x2, f16x2>::type T2;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const T2 h = __builtin_convertvector((f32x2){p[2 * k], p[2 * k + 1]}, T2);
+    hi[k] = __builtin_bit_cast(uint32_t, h);
+    if constexpr (std::is_same<T, __bf16>::value) {
+      // a bf16 is the upper half of an fp32: widen both halves exactly, take the rest
+      const float h0 = __uint_as_float(hi[k] << 16), h1 = __uint_as_float(hi[k] & 0xFFFF0000u);
+      const T2 l = __builtin_convertvector((f32x2){p[2 * k] - h0, p[2 * k + 1] - h1}, T2);
+      lo[k] = __builtin_bit_cast(uint32_t, l);
+    }
+  }
 }
 
 template <typename T>
@@ -192,7 +229,11 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
   const T* vbase = (const T*)P.v_cache + (int64_t)g * tile;
   const int32_t* tbl = P.block_tables + (int64_t)s * P.max_blocks;
 
-  // ---- this lane's rows: query fragments and causal limits
+  // ---- this lane's rows: query fragments and causal limits.  A negative scale is
+  // applied as |scale| to queries with their sign bits flipped (exact), so that the
+  // largest logit is the largest raw dot product.
+  const float sc = fabsf(P.scale_log2);
+  const uint32_t qsign = P.scale_log2 < 0.f ? (sizeof(T) == 2 ? 0x80008000u : 0x80000000u) : 0u;
   u32x4 qf[NTILE][KL];
   int lim[NTILE];
   bool rvalid[NTILE];
@@ -208,7 +249,8 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
     const T* qp = (const T*)P.q + orow[t] * D + quad * EPL;
 #pragma unroll
     for (int c = 0; c < KL; ++c)
-      qf[t][c] = rvalid[t] ? *reinterpret_cast<const u32x4*>(qp + c * 4 * EPL) : u32x4{0u, 0u, 0u, 0u};
+      qf[t][c] = rvalid[t] ? (*reinterpret_cast<const u32x4*>(qp + c * 4 * EPL) ^ qsign)
+                           : u32x4{0u, 0u, 0u, 0u};
   }
 
   // ---- chunk loading, block ids one chunk ahead of the data.  Key piece p (of a
@@ -226,8 +268,10 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
   int kid[SH::KP][NBK], vid[SH::VP];
   u32x4 kr[SH::KP];
   VPiece vr[SH::VP];
-  auto block_id = [&](int j) {  // wave-uniform table read; ids outside the pool -> 0
-    const int id = tbls[min(j, last_blk)];
+  // table reads go out one chunk before their ids are used, and are checked only then,
+  // so that the wait for them falls long after they arrived
+  auto block_id = [&](int j) { return tbls[min(j, last_blk)]; };
+  auto checked = [&](int id) {  // ids outside the pool -> 0, and the workgroup's rows NaN
     const bool ok = (uint32_t)id < nblk32;
     bad |= !ok;
     return ok ? id : 0;
@@ -249,8 +293,11 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
     for (int i = 0; i < SH::KP; ++i) {
       const int p = tid + THREADS * i;
       const int t = p / SH::KSEG;  // (t0 + t) % BS == t % BS: chunks start on block edges
-      int id = kid[i][0];
-      if constexpr (NBK == 2) id = ((t % TPI) >= BS) ? kid[i][1] : kid[i][0];
+      int id = checked(kid[i][0]);
+      if constexpr (NBK == 2) {
+        const int id1 = checked(kid[i][1]);
+        id = ((t % TPI) >= BS) ? id1 : id;
+      }
       const T* blk = kbase + (int64_t)id * blk_stride;
       kr[i] = *reinterpret_cast<const u32x4*>(blk + (t % BS) * D + (p % SH::KSEG) * EPL);
     }
@@ -258,7 +305,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
     for (int i = 0; i < SH::VP; ++i) {
       const int p = tid + THREADS * i;
       const int tk = (p / D) * SH::VPE;
-      const T* blk = vbase + (int64_t)vid[i] * blk_stride;
+      const T* blk = vbase + (int64_t)checked(vid[i]) * blk_stride;
       vr[i] = *reinterpret_cast<const VPiece*>(blk + (p % D) * BS + tk % BS);
     }
   };
@@ -340,28 +387,30 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
     const T* vrow = &sv[buf][col * SH::VROW + 8 * quad];  // dimension 16nn + col, tokens 8quad..
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
-      float z[8];
+      float z[8];  // raw dot products; the scale is applied inside the exponent
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        z[e] = sa[t][e] * P.scale_log2;
-        z[4 + e] = sb[t][e] * P.scale_log2;
+        z[e] = sa[t][e];
+        z[4 + e] = sb[t][e];
       }
       if (masked) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) z[e] = (tfirst + e <= lim[t]) ? z[e] : -INFINITY;
       }
-      float cm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                       fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-      cm = max_over_quads(cm);
-      // every row sees position 0, so after the first chunk m_run is finite
-      const float m_new = fmaxf(m_run[t], cm);
+      const float cm = max_over_quads(max8(z));
+      // every row sees position 0, so after the first chunk m_run is finite (a row with
+      // every position of this chunk masked keeps its maximum: max(m, NaN or -inf) = m)
+      const float m_new = fmaxf(m_run[t], cm * sc);
       const float alpha = exp2_fast(m_run[t] - m_new);
       float pr[8], psum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pr[e] = exp2_fast(z[e] - m_new);
-        psum += pr[e];
+      for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(__builtin_fmaf(z[e], sc, -m_new));
+      if (masked) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pr[e] = (tfirst + e <= lim[t]) ? pr[e] : 0.f;
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) psum += pr[e];
       l_run[t] = l_run[t] * alpha + psum;
       m_run[t] = m_new;
       // after the first chunks the running maximum rarely moves: rescale only when it
@@ -371,22 +420,18 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
         for (int nn = 0; nn < NT; ++nn) acc[t][nn] *= alpha;
       }
       if constexpr (sizeof(T) == 2) {
+        // bf16 keeps 8 significant bits: the weights go in as a hi + lo pair (two
+        // MFMAs), about fp32 accuracy, so that the output's own rounding is the only
+        // visible error; fp16's 11 bits need one rounding only
         typedef typename V8<T>::type VT;
-        VT phi, plo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const T h = (T)pr[e];
-          phi[e] = h;
-          // bf16 keeps 8 significant bits: the weights go in as a hi + lo pair (two
-          // MFMAs), about fp32 accuracy, so that the output's own rounding is the
-          // only visible error; fp16's 11 bits need one rounding only
-          if constexpr (std::is_same<T, __bf16>::value) plo[e] = (T)(pr[e] - (float)h);
-        }
+        u32x4 phi, plo;
+        split_weights<T>(pr, phi, plo);
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn) {
           const VT vv = *reinterpret_cast<const VT*>(vrow + 16 * nn * SH::VROW);
-          acc[t][nn] = mma16(vv, phi, acc[t][nn]);
-          if constexpr (std::is_same<T, __bf16>::value) acc[t][nn] = mma16(vv, plo, acc[t][nn]);
+          acc[t][nn] = mma16(vv, __builtin_bit_cast(VT, phi), acc[t][nn]);
+          if constexpr (std::is_same<T, __bf16>::value)
+            acc[t][nn] = mma16(vv, __builtin_bit_cast(VT, plo), acc[t][nn]);
         }
       } else {
 #pragma unroll
