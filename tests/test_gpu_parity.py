@@ -360,3 +360,46 @@ def test_more_sequences_than_one_launch_plans():
                           max_blocks_per_seq=40, lens=("loguniform", 1, 640))
     _parity(b, what="1100 sequences")
     _parity(b, partition_size=64, what="1100 sequences, 64-token partitions")
+
+
+# ------------------------------------------------------------------ default partitioning
+
+@pytest.mark.parametrize("lens,hq,hkv", [
+    ([20000, 17000, 23456], 32, 8),          # dozens of partitions, two-level merges
+    ([1, 2, 3], 8, 8),                        # fewer items than workgroups
+    ([4096] + [1] * 40 + [700] * 3, 64, 8),   # one long sequence among many one-chunk ones
+    ([5000, 33, 0, 64, 9000], 160, 8),        # two head tiles per KV head, an empty sequence
+])
+def test_default_partitioning_parity(lens, hq, hkv):
+    b = inputs.make_batch("gqa_bf16", seed=21, num_seqs=len(lens), num_q_heads=hq,
+                          num_kv_heads=hkv, max_blocks_per_seq=(max(lens) + 15) // 16 + 1,
+                          lens=("fixed", lens), cache_write=False)
+    _parity(b, partition_size=0, what=f"default partitioning lens={lens[:4]}...")
+
+
+def test_default_partitioning_workspace_reuse_is_bit_stable():
+    """With the default partitioning one workspace serves calls of different shapes, its
+    counters are zero after every call, and repeated calls give the same bits."""
+    import paged_kv_cache_344_amd as pa
+    big = inputs.make_batch("gqa_bf16", seed=22, num_seqs=6, max_blocks_per_seq=700,
+                            lens=("fixed", [1, 11000, 512, 5000, 33, 9000]), cache_write=False)
+    small = inputs.make_batch("gqa_bf16", seed=23, num_seqs=3, max_blocks_per_seq=300,
+                              lens=("fixed", [4000, 70, 4700]), cache_write=False)
+    gb, gs = OnGpu(big), OnGpu(small)
+    ws = pa.workspace_for(gb.q, gb.block_tables, big.num_blocks, big.block_size, big.num_kv_heads)
+    first = {}
+    for rep in range(3):
+        for b, g in ((big, gb), (small, gs)):
+            say(f"default reuse rep {rep} S={b.num_seqs}")
+            out = torch.empty_like(g.q)
+            pa.pa_decode(g.q, g.k_cache, g.v_cache, g.block_tables, g.seq_lens, b.block_size,
+                         b.num_kv_heads, b.scale, out, workspace=ws)
+            torch.cuda.synchronize()
+            nctr = _counter_bytes(b, 0)
+            assert int(torch.count_nonzero(ws[:nctr])) == 0, "counters not zero after the call"
+            got = g.out_f64(out)
+            if rep == 0:
+                check_close(got, oracle_decode(b), "bf16", f"default reuse S={b.num_seqs}")
+                first[b.num_seqs] = got
+            else:
+                np.testing.assert_array_equal(got, first[b.num_seqs])
