@@ -218,7 +218,7 @@ def parity(out, ref, dtype):
 
 def source_digest():
     h = hashlib.sha256()
-    for f in ("decode.hip", "cache_write.hip", "kernels.h"):
+    for f in ("decode.hip", "decode_common.h", "cache_write.hip", "kernels.h"):
         h.update(open(os.path.join(ROOT, "paged_kv_cache_344_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
