@@ -61,7 +61,7 @@ typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = 1, /* a null pointer, a bad size, a misaligned pointer       */
   PA_ERR_UNSUPPORTED = 2, /* valid but not built: dtype / head_dim / block_size ... */
-  PA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required       */
+  PA_ERR_WORKSPACE = 3,   /* a workspace missing or smaller than required            */
   PA_ERR_HIP = 4,         /* the HIP runtime refused a launch; see pa_last_error()   */
   PA_ERR_CAPACITY = 5     /* block manager: no free block, or a table would overflow */
 } pa_status;
@@ -200,7 +200,12 @@ typedef struct pa_multi_token_ext {
   int32_t head_dim;           /* D: 64 or 128                                          */
   int32_t max_blocks_per_seq; /* row stride of block_tables, >= 1                      */
   int64_t num_blocks;         /* N, physical blocks in the pool, >= 1                  */
+  int32_t partition_size;     /* context split: 0 = automatic, < 0 = never split,      */
+                              /* > 0 = that many tokens per partition (multiple of 32) */
   int32_t dtype;              /* pa_dtype of q, k_cache, v_cache and out               */
+  void* workspace;            /* device scratch for split partials, caller-owned;      */
+                              /* unused (may be NULL) when the call does not split     */
+  size_t workspace_bytes;     /* its size; see pa_multi_token_workspace_bytes          */
   void* stream;               /* hipStream_t                                           */
 } pa_multi_token_ext;
 
@@ -234,15 +239,47 @@ typedef struct pa_multi_token_ext {
  * skipped; one with n_s > L_s or L_s > max_blocks_per_seq * bs, or a bad table entry,
  * gets NaN rows; rows past max_query_len are not written.
  *
- * One launch, asynchronous on ext->stream, no device memory of its own.  Errors:
+ * Context split.  With few (sequence, KV head, 128-row tile) triples, e.g. a few draft
+ * tokens per sequence over long contexts, one workgroup per triple leaves most of the
+ * device idle.  The call then cuts every sequence's positions into partitions of
+ * part_tokens positions, computes each partition's rows (running maximum, running
+ * sum, unnormalised output) into the workspace and combines them with log-sum-exp
+ * weights in partition order in a second launch: deterministic, and equal to the
+ * unsplit result up to fp32 rounding.  partition_size > 0 fixes part_tokens; 0 picks
+ * it from the shapes alone (rows per tile, table capacity max_blocks_per_seq * bs,
+ * the number of triples): a split only when there are fewer than 512 triples and
+ * partitions of at least max(256, 16 * rows per tile) tokens, and then about 512
+ * workgroups.  The automatic choice assumes sequences near the table's capacity;
+ * callers that know shorter lengths pass partition_size.
+ *
+ * Workspace (ext->workspace, ext->workspace_bytes): device memory owned by the
+ * caller, of at least pa_multi_token_workspace_bytes bytes when the call splits (0
+ * otherwise: workspace may then be NULL).  Scratch only: no zero-fill is needed, and
+ * calls of any shapes may share it as long as they are ordered on one stream (calls
+ * that overlap on one workspace race).
+ *
+ * Asynchronous on ext->stream: one launch, or two when the call splits.  Errors:
  * PA_ERR_INVALID_ARG for NULL or misaligned pointers, bad shapes or dtype, a
- * non-finite scale; PA_ERR_UNSUPPORTED for a head_dim or block_size not built or a
- * launch too large; PA_ERR_HIP if the launch fails.
+ * non-finite scale, a partition_size that is not a multiple of 32; PA_ERR_WORKSPACE
+ * for a split call whose workspace is missing or too small; PA_ERR_UNSUPPORTED for a
+ * head_dim or block_size not built or a launch too large; PA_ERR_HIP if a launch
+ * fails.
  */
 pa_status pa_multi_token(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* seq_lens,
                          const int32_t* query_start, int32_t block_size, int32_t num_kv_heads,
                          float scale, void* out, const pa_multi_token_ext* ext);
+
+/*
+ * pa_multi_token_workspace_bytes - bytes of workspace a pa_multi_token call with these
+ * shapes needs: 0 when it does not split, else S * Hkv * tiles * parts * rows * (D + 2)
+ * * 4, tiles = ceil(max_query_len * G / 128), rows = min(128, max_query_len * G),
+ * parts = ceil(max_blocks_per_seq * bs / part_tokens).  Only the shape fields of ext
+ * are read.  Returns PA_OK and sets *bytes, or the error status pa_multi_token would
+ * report for the same shapes.
+ */
+pa_status pa_multi_token_workspace_bytes(const pa_multi_token_ext* ext, int32_t block_size,
+                                         int32_t num_kv_heads, size_t* bytes);
 
 /* Shapes of a pa_copy_blocks call. */
 typedef struct pa_copy_blocks_ext {

@@ -44,8 +44,9 @@ class MultiTokenExt(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
                 ("max_query_len", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
-                ("num_blocks", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("stream", ctypes.c_void_p)]
+                ("num_blocks", ctypes.c_int64), ("partition_size", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p)]
 
 
 class CopyBlocksExt(ctypes.Structure):
@@ -77,6 +78,9 @@ def lib():
         L.pa_multi_token.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp,
                                      ctypes.POINTER(MultiTokenExt)]
         L.pa_multi_token.restype = ctypes.c_int
+        L.pa_multi_token_workspace_bytes.argtypes = [ctypes.POINTER(MultiTokenExt), i32, i32,
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+        L.pa_multi_token_workspace_bytes.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(CopyBlocksExt)]
         L.pa_copy_blocks.restype = ctypes.c_int
         P32, P64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -285,7 +289,8 @@ class PreparedMultiToken:
     def __init__(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  block_tables: torch.Tensor, seq_lens: torch.Tensor, query_start: torch.Tensor,
                  block_size: int, num_kv_heads: int, scale: float, out: torch.Tensor, *,
-                 max_query_len: int, stream=None):
+                 max_query_len: int, partition_size: int = 0,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
         dev = q.device
         _need(dev.type == "cuda", "tensors must be on a GPU")
         for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
@@ -308,11 +313,23 @@ class PreparedMultiToken:
         _need(block_tables.dim() == 2 and block_tables.shape[0] == S, "block_tables shape")
         _need(query_start.shape == (S + 1,), "query_start shape")
         _need(out.shape == q.shape, "out shape")
-        self.ext = MultiTokenExt(num_seqs=S, num_tokens=T, max_query_len=max_query_len,
-                                 num_q_heads=Hq, head_dim=D,
-                                 max_blocks_per_seq=block_tables.shape[1], num_blocks=N,
-                                 dtype=TORCH_DTYPE[q.dtype], stream=_stream_ptr(dev, stream))
-        self.tensors = (q, k_cache, v_cache, block_tables, seq_lens, query_start, out)
+        ext = MultiTokenExt(num_seqs=S, num_tokens=T, max_query_len=max_query_len,
+                            num_q_heads=Hq, head_dim=D, max_blocks_per_seq=block_tables.shape[1],
+                            num_blocks=N, partition_size=partition_size,
+                            dtype=TORCH_DTYPE[q.dtype])
+        need = ctypes.c_size_t(0)
+        _check(lib().pa_multi_token_workspace_bytes(ctypes.byref(ext), block_size, num_kv_heads,
+                                                    ctypes.byref(need)), "pa_multi_token")
+        self.workspace_bytes = need.value
+        if workspace is None and need.value:
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)  # scratch
+        if workspace is not None:
+            _need(workspace.device == dev and workspace.is_contiguous(), "workspace placement")
+            ext.workspace = workspace.data_ptr()
+            ext.workspace_bytes = workspace.numel() * workspace.element_size()
+        ext.stream = _stream_ptr(dev, stream)
+        self.ext = ext
+        self.tensors = (q, k_cache, v_cache, block_tables, seq_lens, query_start, out, workspace)
         self.out = out
         self._fn = lib().pa_multi_token
         self._args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -330,13 +347,19 @@ class PreparedMultiToken:
 def pa_multi_token(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                    block_tables: torch.Tensor, seq_lens: torch.Tensor, query_start: torch.Tensor,
                    block_size: int, num_kv_heads: int, scale: float, out: torch.Tensor, *,
-                   max_query_len: int, stream=None) -> torch.Tensor:
+                   max_query_len: int, partition_size: int = 0,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Attention for several new tokens per sequence (see include/pa.h): q, out
     [T, Hq, D]; query_start int32 [S+1] on the GPU; ``max_query_len`` >= every
-    sequence's number of new tokens (a host value: it sizes the launch)."""
+    sequence's number of new tokens (a host value: it sizes the launch).
+    ``partition_size``: 0 splits the context automatically when the launch would be
+    small, < 0 never, > 0 into partitions of that many tokens.  A split call needs a
+    byte tensor of ``pa_multi_token_workspace_bytes`` bytes (scratch, no zero-fill);
+    when omitted, one is allocated for this call."""
     return PreparedMultiToken(q, k_cache, v_cache, block_tables, seq_lens, query_start,
                               block_size, num_kv_heads, scale, out,
-                              max_query_len=max_query_len, stream=stream)()
+                              max_query_len=max_query_len, partition_size=partition_size,
+                              workspace=workspace, stream=stream)()
 
 
 class PreparedCopyBlocks:

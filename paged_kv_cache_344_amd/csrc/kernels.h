@@ -75,6 +75,11 @@ struct MultiTokenParams {
   int32_t max_blocks;           // row stride of block_tables
   int32_t max_tokens;           // max_blocks * bs
   int32_t row_tiles;            // workgroup row tiles per (sequence, KV head)
+  int32_t parts;                // context partitions per (sequence, KV head); 1: no split
+  int32_t part_tokens;          // tokens per partition, a multiple of 32
+  int32_t part_rows;            // rows stored per (row tile, partition): min(128, rows)
+  float* part_o;                // [S][Hkv][row_tiles][parts][part_rows][D] unnormalised outputs
+  float* part_ml;               // [S][Hkv][row_tiles][parts][part_rows][2] (max in log2 units, sum)
   float scale_log2;             // scale * log2(e)
 };
 
@@ -101,5 +106,8 @@ hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
 int multi_token_rows_per_group();
 hipError_t launch_multi_token(int dtype, int head_dim, int block_size, MultiTokenParams p,
                               hipStream_t stream);
+// The log-sum-exp combination of a split launch's partitions into out.
+hipError_t launch_multi_token_merge(int dtype, int head_dim, const MultiTokenParams& p,
+                                    hipStream_t stream);
 
 }  // namespace pa

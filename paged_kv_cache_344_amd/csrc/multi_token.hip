@@ -38,7 +38,13 @@
 // output's own rounding), rounded once for fp16, and exactly for fp32; the sum that
 // normalises them is kept in fp32.
 //
-// Launch.  One workgroup per (row tile, KV head, sequence).  Workgroups are dispatched
+// Context split.  With few (row tile, KV head, sequence) triples, as when a few draft
+// tokens per sequence are verified against long contexts, the tokens of each sequence
+// are cut into partitions of part_tokens positions, one workgroup each; every
+// workgroup leaves its rows' running maximum, sum and unnormalised output in a
+// workspace, and a second launch combines them with log-sum-exp weights.
+//
+// Launch.  One workgroup per (row tile, partition, KV head, sequence).  Workgroups are dispatched
 // to the eight XCDs in turn; the numbering deals whole (sequence, KV head) groups to
 // the XCDs round-robin, so that the row tiles of a group share their XCD's L2 copy of
 // the K/V they all read, and every XCD gets a share of every sequence.
@@ -181,15 +187,19 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
   __shared__ __attribute__((aligned(16))) T sk[2][CH * SH::KROW];
   __shared__ __attribute__((aligned(16))) T sv[2][D * SH::VROW];
 
-  // ---- which (row tile, KV head, sequence): (sequence, KV head) groups are dealt to
-  // the XCDs in turn, and every row tile of a group runs on its group's XCD
+  // ---- which (row tile, context partition, KV head, sequence): (sequence, KV head)
+  // groups are dealt to the XCDs in turn, and every row tile and partition of a group
+  // runs on its group's XCD
+  const int per_group = P.row_tiles * P.parts;
   const int xcd = (int)(blockIdx.x % XCDS);
   const int idx = (int)(blockIdx.x / XCDS);
-  const int group = (idx / P.row_tiles) * XCDS + xcd;
+  const int group = (idx / per_group) * XCDS + xcd;
   if (group >= P.num_kv_heads * P.num_seqs) return;
   const int x = idx % P.row_tiles;
+  const int part = (idx % per_group) / P.row_tiles;
   const int g = group % P.num_kv_heads;
   const int s = group / P.num_kv_heads;
+  const bool split = P.parts > 1;
 
   const int G = P.group, Hq = P.num_q_heads;
   const int q0 = P.query_start[s], q1 = P.query_start[s + 1];
@@ -209,6 +219,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
   const int quad = lane >> 4;
 
   if (L > P.max_tokens || n > L) {  // a length the table cannot hold: NaN rows
+    if (split) return;                // (the merge writes them)
     for (int i = tid; i < (rend - R0) * D; i += THREADS) {
       const int rr = R0 + i / D;
       const int64_t row = (int64_t)(q0 + rr / G) * Hq + g * G + rr % G;
@@ -219,7 +230,10 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
   const int ctx = L - n;
   const int lim_lo = ctx + R0 / G;          // the earliest causal limit among these rows
   const int lim_hi = ctx + (rend - 1) / G;  // the latest
-  const int nch = lim_hi / CH + 1;
+  // this workgroup's chunks: c_lo .. nch-1 of the 0 .. lim_hi / CH its rows may see
+  const int c_lo = part * (P.part_tokens / CH);
+  const int nch = split ? min(lim_hi / CH + 1, c_lo + P.part_tokens / CH) : lim_hi / CH + 1;
+  if (c_lo >= nch) return;  // a partition past these rows' positions: the merge skips it
   const int last_blk = (L - 1) / BS;
 
   const uint32_t nblk32 = (uint32_t)min(P.num_blocks, (int64_t)0x7fffffff);
@@ -398,13 +412,16 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
         for (int e = 0; e < 8; ++e) z[e] = (tfirst + e <= lim[t]) ? z[e] : -INFINITY;
       }
       const float cm = max_over_quads(max8(z));
-      // every row sees position 0, so after the first chunk m_run is finite (a row with
-      // every position of this chunk masked keeps its maximum: max(m, NaN or -inf) = m)
+      // a row with every position of this chunk masked keeps its maximum (max(m, -inf)
+      // = m); while it has seen no position at all (a partition that starts past its
+      // causal limit) the maximum stays -inf and is taken as 0 in the exponents, so that
+      // its weights and rescale factor are exp2(-inf) = 0, never exp2(-inf + inf)
       const float m_new = fmaxf(m_run[t], cm * sc);
-      const float alpha = exp2_fast(m_run[t] - m_new);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2_fast(m_run[t] - m_use);
       float pr[8], psum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(__builtin_fmaf(z[e], sc, -m_new));
+      for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(__builtin_fmaf(z[e], sc, -m_use));
       if (masked) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) pr[e] = (tfirst + e <= lim[t]) ? pr[e] : 0.f;
@@ -447,13 +464,13 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
     }
   };
 
-  // ---- the chunk pipeline
-  load_ids(0, kid, vid);
+  // ---- the chunk pipeline over chunks c_lo .. nch-1
+  load_ids(c_lo, kid, vid);
   load_data();
-  store_lds(0, 0);
-  if (nch > 1) load_ids(1, kid, vid);
+  store_lds(c_lo, c_lo & 1);
+  if (c_lo + 1 < nch) load_ids(c_lo + 1, kid, vid);
   __syncthreads();
-  for (int c = 0; c < nch; ++c) {
+  for (int c = c_lo; c < nch; ++c) {
     const int buf = c & 1;
     if (c + 1 < nch) load_data();
     int kid2[SH::KP][NBK], vid2[SH::VP];
@@ -472,6 +489,27 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
   }
   bad = __syncthreads_or(bad);
 
+  if (split) {
+    // this partition's partial rows for the merge: running maximum (log2 units), sum
+    // and unnormalised output; a bad table entry makes them NaN
+    const int64_t tile0 =
+        ((((int64_t)s * P.num_kv_heads + g) * P.row_tiles + x) * P.parts + part) * P.part_rows;
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+      const float l = sum_over_quads(l_run[t]);
+      if (!rvalid[t]) continue;
+      const int64_t r = tile0 + wave * (NTILE * 16) + t * 16 + col;
+      float* po = P.part_o + r * D + 4 * quad;
+#pragma unroll
+      for (int nn = 0; nn < NT; ++nn)
+        *reinterpret_cast<f32x4*>(po + 16 * nn) = bad ? f32x4{nan, nan, nan, nan} : acc[t][nn];
+      if (quad == 0)
+        *reinterpret_cast<f32x2*>(P.part_ml + 2 * r) = bad ? f32x2{nan, nan} : f32x2{m_run[t], l};
+    }
+    return;
+  }
+
   // ---- normalise and store
 #pragma unroll
   for (int t = 0; t < NTILE; ++t) {
@@ -484,6 +522,58 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
       if (bad) v = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
       store4(o + 16 * nn, v);
     }
+  }
+}
+
+// The merge after a split launch: one workgroup per (row tile, KV head, sequence)
+// combines each row's partitions with log-sum-exp weights, in partition order, and
+// writes the output row (NaN rows for a length the table cannot hold).  Partitions that
+// start past the tile's last causal limit were skipped by the main kernel; the first
+// partition always holds position 0, which every row sees.
+template <typename T, int D>
+__global__ __launch_bounds__(THREADS) void multi_token_merge_kernel(MultiTokenParams P) {
+  const int x = (int)(blockIdx.x % P.row_tiles);
+  const int group = (int)(blockIdx.x / P.row_tiles);
+  const int g = group % P.num_kv_heads;
+  const int s = group / P.num_kv_heads;
+  const int G = P.group, Hq = P.num_q_heads;
+  const int q0 = P.query_start[s], q1 = P.query_start[s + 1];
+  const int n = q1 - q0;
+  if (q0 < 0 || n < 0 || q1 > P.num_tokens) return;
+  const int R0 = x * ROWS;
+  const int rend = min(n * G, R0 + ROWS);
+  if (R0 >= rend) return;
+  const int L = P.seq_lens[s];
+  const bool invalid = L > P.max_tokens || n > L;
+  const int lim_hi = L - n + (rend - 1) / G;
+  const int used = min(P.parts, (lim_hi / CH) / (P.part_tokens / CH) + 1);
+  const int64_t tile0 = (((int64_t)s * P.num_kv_heads + g) * P.row_tiles + x) * P.parts * P.part_rows;
+  const int64_t pstride = P.part_rows;
+  for (int it = threadIdx.x; it < (rend - R0) * (D / 4); it += THREADS) {
+    const int r = it / (D / 4);
+    const int d4 = (it - r * (D / 4)) * 4;
+    const int rr = R0 + r;
+    T* o = (T*)P.out + ((int64_t)(q0 + rr / G) * Hq + g * G + rr % G) * D + d4;
+    if (invalid) {
+      const float nan = __builtin_nanf("");
+      store4(o, f32x4{nan, nan, nan, nan});
+      continue;
+    }
+    float M = -INFINITY;
+    for (int p = 0; p < used; ++p) M = fmaxf(M, P.part_ml[2 * (tile0 + p * pstride + r)]);
+    float Ls = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    bool nan_seen = false;
+    for (int p = 0; p < used; ++p) {
+      const int64_t pr = tile0 + p * pstride + r;
+      const f32x2 ml = *reinterpret_cast<const f32x2*>(P.part_ml + 2 * pr);
+      nan_seen |= ml[0] != ml[0];
+      const float w = exp2_fast(ml[0] - M);  // 0 for a partition none of whose positions the row sees
+      Ls += w * ml[1];
+      O += w * *reinterpret_cast<const f32x4*>(P.part_o + pr * D + d4);
+    }
+    const float nan = __builtin_nanf("");
+    store4(o, nan_seen ? f32x4{nan, nan, nan, nan} : O / Ls);
   }
 }
 
@@ -516,16 +606,45 @@ const void* multi_token_kernel_for(int dtype, int head_dim, int block_size) {
   return nullptr;
 }
 
+template <typename T>
+const void* merge_d(int d) {
+  switch (d) {
+    case 64: return (const void*)multi_token_merge_kernel<T, 64>;
+    case 128: return (const void*)multi_token_merge_kernel<T, 128>;
+  }
+  return nullptr;
+}
+
+const void* multi_token_merge_for(int dtype, int head_dim) {
+  switch (dtype) {
+    case 0: return merge_d<float>(head_dim);
+    case 1: return merge_d<_Float16>(head_dim);
+    case 2: return merge_d<__bf16>(head_dim);
+  }
+  return nullptr;
+}
+
 }  // namespace
 
 int multi_token_rows_per_group() { return ROWS; }
+
+hipError_t launch_multi_token_merge(int dtype, int head_dim, const MultiTokenParams& p,
+                                    hipStream_t stream) {
+  const void* k = multi_token_merge_for(dtype, head_dim);
+  const int64_t grid = (int64_t)p.row_tiles * p.num_kv_heads * p.num_seqs;
+  if (!k || grid <= 0 || grid > 0x7fffffff || p.parts < 2) return hipErrorInvalidValue;
+  MultiTokenParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(k, dim3((unsigned)grid), dim3(THREADS), args, 0, stream);
+}
 
 hipError_t launch_multi_token(int dtype, int head_dim, int block_size, MultiTokenParams p,
                               hipStream_t stream) {
   const void* k = multi_token_kernel_for(dtype, head_dim, block_size);
   const int64_t groups = (int64_t)p.num_kv_heads * p.num_seqs;
-  const int64_t per_xcd = (groups + XCDS - 1) / XCDS * p.row_tiles;
-  if (!k || groups <= 0 || p.row_tiles <= 0 || per_xcd * XCDS > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t per_xcd = (groups + XCDS - 1) / XCDS * p.row_tiles * p.parts;
+  if (!k || groups <= 0 || p.row_tiles <= 0 || p.parts <= 0 || per_xcd * XCDS > 0x7fffffff)
+    return hipErrorInvalidValue;
   void* args[] = {&p};
   return hipLaunchKernel(k, dim3((unsigned)(per_xcd * XCDS)), dim3(THREADS), args, 0, stream);
 }

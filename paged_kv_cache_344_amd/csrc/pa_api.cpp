@@ -3,8 +3,9 @@
 // Every host-side argument is checked before the first HIP call, so a bad call
 // returns a status without touching the GPU (and can be tested on a machine with
 // none).  The library owns no device memory: the decode workspace (work queue,
-// merge counters, split-K partials) is the caller's, sized by
-// pa_decode_workspace_bytes.
+// merge counters, split-K partials) and the multi-token one (context-split partials)
+// are the caller's, sized by pa_decode_workspace_bytes and
+// pa_multi_token_workspace_bytes.
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -144,6 +145,84 @@ pa_status decode_grid(int dtype, int D, int bs, int* grid) {
   return PA_OK;
 }
 
+
+// Shapes of a pa_multi_token call, checked, and its context split.
+struct MtPlan {
+  bool empty = false;       // nothing to compute
+  int32_t max_tokens = 0;   // max_blocks_per_seq * bs
+  int32_t tiles = 0;        // 128-row tiles per (sequence, KV head)
+  int32_t parts = 1;        // context partitions (1: no split)
+  int32_t part_tokens = 0;  // positions per partition
+  int32_t part_rows = 0;    // rows stored per (tile, partition)
+  int64_t partial_rows = 0; // rows of partials in the workspace
+  size_t ws_bytes = 0;
+};
+
+pa_status plan_multi_token(const pa_multi_token_ext* ext, int32_t bs, int32_t hkv, MtPlan* pl) {
+  if (!ext) return fail(PA_ERR_INVALID_ARG, "ext is NULL");
+  const int32_t S = ext->num_seqs, T = ext->num_tokens, Hq = ext->num_q_heads, D = ext->head_dim;
+  const int32_t MB = ext->max_blocks_per_seq;
+  if (S < 0 || S > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d outside [0, 65535]", S);
+  if (T < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %d < 0", T);
+  if (ext->max_query_len < 0) return fail(PA_ERR_INVALID_ARG, "max_query_len %d < 0", ext->max_query_len);
+  if (Hq <= 0) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d <= 0", Hq);
+  if (hkv <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d <= 0", hkv);
+  if (Hq % hkv) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", Hq, hkv);
+  if (D <= 0) return fail(PA_ERR_INVALID_ARG, "head_dim %d <= 0", D);
+  if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", D);
+  if (bs <= 0) return fail(PA_ERR_INVALID_ARG, "block_size %d <= 0", bs);
+  if (!block_size_built(bs)) return fail(PA_ERR_UNSUPPORTED, "block_size %d (built: 4, 8, 16, 32)", bs);
+  if (MB <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d <= 0", MB);
+  if (ext->num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks %lld <= 0", (long long)ext->num_blocks);
+  if (!dtype_valid(ext->dtype)) return fail(PA_ERR_INVALID_ARG, "dtype %d", ext->dtype);
+  const int64_t max_tokens = (int64_t)MB * bs;
+  if (max_tokens > (int64_t(1) << 30)) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size too large");
+  const int32_t psz = ext->partition_size;
+  if (psz > 0 && psz % 32) return fail(PA_ERR_INVALID_ARG, "partition_size %d is not a multiple of 32", psz);
+  pl->max_tokens = (int32_t)max_tokens;
+  if (S == 0 || T == 0 || ext->max_query_len == 0) {
+    pl->empty = true;
+    return PA_OK;
+  }
+  const int32_t G = Hq / hkv;
+  const int64_t R = pa::multi_token_rows_per_group();
+  const int64_t rows = (int64_t)std::min(ext->max_query_len, T) * G;
+  const int64_t tiles = (rows + R - 1) / R;
+  if ((int64_t)T * G > (int64_t)INT32_MAX - 1024 || (int64_t)T * Hq * D > ((int64_t)1 << 40))
+    return fail(PA_ERR_UNSUPPORTED, "num_tokens %d too large for one launch", T);
+  const int64_t triples = (int64_t)S * hkv * tiles;
+  const int64_t part_rows = std::min(R, rows);
+  int64_t part_tokens = 0;
+  if (psz > 0) {
+    part_tokens = psz;
+  } else if (psz == 0) {
+    // about 512 workgroups (two per CU), partitions long enough that their partials
+    // ((D + 2) * 4 bytes per row) stay small next to the K/V they replace (2 * D * 2
+    // bytes per position): at least 16 positions per stored row
+    const int64_t min_part = std::max<int64_t>(256, (16 * part_rows + 31) / 32 * 32);
+    const int64_t want = (512 + triples - 1) / triples;
+    const int64_t fit = max_tokens / min_part;
+    const int64_t parts = std::min(want, fit);
+    if (triples < 512 && parts >= 2) part_tokens = ((max_tokens + parts - 1) / parts + 31) / 32 * 32;
+  }
+  int64_t parts = part_tokens > 0 ? (max_tokens + part_tokens - 1) / part_tokens : 1;
+  if (parts <= 1) {
+    parts = 1;
+    part_tokens = 0;
+  }
+  const int64_t wgs = (((int64_t)S * hkv + 7) / 8 * 8) * tiles * parts;  // groups dealt to 8 XCDs
+  if (wgs > (int64_t)INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "%lld workgroups in one launch", (long long)wgs);
+  pl->tiles = (int32_t)tiles;
+  pl->parts = (int32_t)parts;
+  pl->part_tokens = (int32_t)part_tokens;
+  pl->part_rows = (int32_t)part_rows;
+  if (parts > 1) {
+    pl->partial_rows = triples * parts * part_rows;
+    pl->ws_bytes = (size_t)pl->partial_rows * (size_t)(D + 2) * sizeof(float);
+  }
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -266,44 +345,40 @@ pa_status pa_cache_write(const void* k, const void* v, const int64_t* slot_mappi
   return PA_OK;
 }
 
+pa_status pa_multi_token_workspace_bytes(const pa_multi_token_ext* ext, int32_t block_size,
+                                         int32_t num_kv_heads, size_t* bytes) {
+  g_error.clear();
+  if (!bytes) return fail(PA_ERR_INVALID_ARG, "bytes is NULL");
+  MtPlan pl;
+  const pa_status st = plan_multi_token(ext, block_size, num_kv_heads, &pl);
+  if (st != PA_OK) return st;
+  *bytes = pl.ws_bytes;
+  return PA_OK;
+}
+
 pa_status pa_multi_token(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* seq_lens,
                          const int32_t* query_start, int32_t block_size, int32_t num_kv_heads,
                          float scale, void* out, const pa_multi_token_ext* ext) {
   g_error.clear();
-  if (!ext) return fail(PA_ERR_INVALID_ARG, "ext is NULL");
-  const int32_t S = ext->num_seqs, T = ext->num_tokens, Hq = ext->num_q_heads, D = ext->head_dim;
-  const int32_t MB = ext->max_blocks_per_seq, bs = block_size, hkv = num_kv_heads;
-  if (S < 0 || S > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d outside [0, 65535]", S);
-  if (T < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %d < 0", T);
-  if (ext->max_query_len < 0) return fail(PA_ERR_INVALID_ARG, "max_query_len %d < 0", ext->max_query_len);
-  if (Hq <= 0) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d <= 0", Hq);
-  if (hkv <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d <= 0", hkv);
-  if (Hq % hkv) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", Hq, hkv);
-  if (D <= 0) return fail(PA_ERR_INVALID_ARG, "head_dim %d <= 0", D);
-  if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", D);
-  if (bs <= 0) return fail(PA_ERR_INVALID_ARG, "block_size %d <= 0", bs);
-  if (!block_size_built(bs)) return fail(PA_ERR_UNSUPPORTED, "block_size %d (built: 4, 8, 16, 32)", bs);
-  if (MB <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d <= 0", MB);
-  if (ext->num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks %lld <= 0", (long long)ext->num_blocks);
-  if (!dtype_valid(ext->dtype)) return fail(PA_ERR_INVALID_ARG, "dtype %d", ext->dtype);
-  const int64_t max_tokens = (int64_t)MB * bs;
-  if (max_tokens > (int64_t(1) << 30)) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size too large");
+  MtPlan pl;
+  const pa_status st = plan_multi_token(ext, block_size, num_kv_heads, &pl);
+  if (st != PA_OK) return st;
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-  if (S == 0 || T == 0 || ext->max_query_len == 0) return PA_OK;
+  if (pl.empty) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start || !out)
     return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
     return fail(PA_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
   if (!aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(query_start, 4))
     return fail(PA_ERR_INVALID_ARG, "block_tables, seq_lens and query_start must be 4-byte aligned");
-  const int32_t G = Hq / hkv;
-  const int64_t rows = (int64_t)std::min(ext->max_query_len, T) * G;
-  const int64_t tiles = (rows + pa::multi_token_rows_per_group() - 1) / pa::multi_token_rows_per_group();
-  const int64_t wgs = ((int64_t)S * hkv + 7) / 8 * 8 * tiles;  // groups dealt to 8 XCDs
-  if (wgs > (int64_t)INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "%lld workgroups in one launch", (long long)wgs);
-  if ((int64_t)T * G > (int64_t)INT32_MAX - 1024 || (int64_t)T * Hq * D > ((int64_t)1 << 40))
-    return fail(PA_ERR_UNSUPPORTED, "num_tokens %d too large for one launch", T);
+  if (pl.parts > 1) {
+    if (!ext->workspace || ext->workspace_bytes < pl.ws_bytes)
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.ws_bytes,
+                  ext->workspace ? ext->workspace_bytes : (size_t)0);
+    if (!aligned(ext->workspace, 16)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  const int32_t hkv = num_kv_heads;
   pa::MultiTokenParams p;
   p.q = q;
   p.k_cache = k_cache;
@@ -313,17 +388,31 @@ pa_status pa_multi_token(const void* q, const void* k_cache, const void* v_cache
   p.query_start = query_start;
   p.out = out;
   p.num_blocks = ext->num_blocks;
-  p.num_seqs = S;
-  p.num_tokens = T;
-  p.num_q_heads = Hq;
+  p.num_seqs = ext->num_seqs;
+  p.num_tokens = ext->num_tokens;
+  p.num_q_heads = ext->num_q_heads;
   p.num_kv_heads = hkv;
-  p.group = G;
-  p.max_blocks = MB;
-  p.max_tokens = (int32_t)max_tokens;
-  p.row_tiles = (int32_t)tiles;
+  p.group = ext->num_q_heads / hkv;
+  p.max_blocks = ext->max_blocks_per_seq;
+  p.max_tokens = pl.max_tokens;
+  p.row_tiles = pl.tiles;
+  p.parts = pl.parts;
+  p.part_tokens = pl.part_tokens;
+  p.part_rows = pl.part_rows;
+  p.part_o = nullptr;
+  p.part_ml = nullptr;
+  if (pl.parts > 1) {
+    p.part_o = static_cast<float*>(ext->workspace);
+    p.part_ml = p.part_o + pl.partial_rows * ext->head_dim;
+  }
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);  // log2(e)
-  const hipError_t e = pa::launch_multi_token(ext->dtype, D, bs, p, static_cast<hipStream_t>(ext->stream));
+  hipStream_t stream = static_cast<hipStream_t>(ext->stream);
+  hipError_t e = pa::launch_multi_token(ext->dtype, ext->head_dim, block_size, p, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "multi-token launch: %s", hipGetErrorString(e));
+  if (pl.parts > 1) {
+    e = pa::launch_multi_token_merge(ext->dtype, ext->head_dim, p, stream);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "multi-token merge launch: %s", hipGetErrorString(e));
+  }
   return PA_OK;
 }
 

@@ -239,3 +239,88 @@ def test_multi_token_nothing_to_do(lib):
     assert _mt(lib, ptr=0, num_seqs=0) == B.PA_OK
     assert _mt(lib, ptr=0, num_tokens=0) == B.PA_OK
     assert _mt(lib, ptr=0, max_query_len=0) == B.PA_OK
+
+
+def _mt_ws(lib, bs=16, hkv=8, **kw):
+    base = dict(num_seqs=4, num_tokens=64, max_query_len=32, num_q_heads=64, head_dim=128,
+                max_blocks_per_seq=64, num_blocks=100, dtype=B.PA_BF16, stream=None)
+    base.update(kw)
+    e = B.MultiTokenExt(**base)
+    n = ctypes.c_size_t(12345)
+    st = lib.pa_multi_token_workspace_bytes(ctypes.byref(e), bs, hkv, ctypes.byref(n))
+    return st, n.value
+
+
+def _mt_expected(S, T, mq, Hq, Hkv, D, MB, bs, psz):
+    """Workspace bytes of the documented context-split policy."""
+    G = Hq // Hkv
+    rows = min(mq, T) * G
+    tiles = -(-rows // 128)
+    part_rows = min(128, rows)
+    triples = S * Hkv * tiles
+    max_tokens = MB * bs
+    if psz > 0:
+        pt = psz
+    elif psz < 0:
+        return 0
+    else:
+        min_part = max(256, -(-16 * part_rows // 32) * 32)
+        parts = min(-(-512 // triples), max_tokens // min_part)
+        if triples >= 512 or parts < 2:
+            return 0
+        pt = -(-(-(-max_tokens // parts)) // 32) * 32
+    parts = -(-max_tokens // pt)
+    if parts < 2:
+        return 0
+    return triples * parts * part_rows * (D + 2) * 4
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),                                                  # 64 triples, short table: no split
+    dict(num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=2048),  # verify: split
+    dict(num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=2048, partition_size=-1),
+    dict(num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=2048, partition_size=96),
+    dict(num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=2048,
+         partition_size=1 << 16),                            # one partition: no split
+    dict(num_seqs=1, max_query_len=40, num_tokens=40, max_blocks_per_seq=512),  # 320 rows, 3 tiles
+    dict(num_seqs=64, max_query_len=4, num_tokens=256, max_blocks_per_seq=2048),  # 512 triples
+    dict(num_seqs=8, max_query_len=2, num_tokens=16, num_q_heads=8, max_blocks_per_seq=100,
+         head_dim=64),                                       # G = 1, 2 rows per tile
+])
+def test_multi_token_workspace_formula(lib, kw):
+    st, n = _mt_ws(lib, **kw)
+    assert st == B.PA_OK
+    a = dict(S=4, T=64, mq=32, Hq=64, D=128, MB=64, psz=0)
+    names = dict(num_seqs="S", num_tokens="T", max_query_len="mq", num_q_heads="Hq",
+                 head_dim="D", max_blocks_per_seq="MB", partition_size="psz")
+    for k, v in kw.items():
+        a[names[k]] = v
+    want = _mt_expected(a["S"], a["T"], a["mq"], a["Hq"], 8, a["D"], a["MB"], 16, a["psz"])
+    assert n == want
+
+
+def test_multi_token_split_examples(lib):
+    # 2 sequences x 8 KV heads x 4 tokens x G 8 = 32 rows: 16 triples, 32768 positions
+    # -> 32 partitions of 1024, 16 * 32 * 32 rows of (128 + 2) floats
+    st, n = _mt_ws(lib, num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=2048)
+    assert st == B.PA_OK and n == 16 * 32 * 32 * 130 * 4
+    st, n = _mt_ws(lib, num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=2048,
+                   partition_size=96)
+    assert st == B.PA_OK and n == 16 * 342 * 32 * 130 * 4
+    st, n = _mt_ws(lib, num_seqs=64, max_query_len=4, num_tokens=256, max_blocks_per_seq=2048)
+    assert st == B.PA_OK and n == 0                          # enough workgroups already
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(partition_size=100), B.PA_ERR_INVALID_ARG),
+    (dict(partition_size=64), B.PA_ERR_WORKSPACE),           # split, no workspace
+    (dict(partition_size=64, workspace=FAKE, workspace_bytes=4096), B.PA_ERR_WORKSPACE),
+    (dict(partition_size=64, workspace=FAKE + 8, workspace_bytes=1 << 40), B.PA_ERR_INVALID_ARG),
+    (dict(num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=2048),
+     B.PA_ERR_WORKSPACE),                                    # automatic split, no workspace
+])
+def test_multi_token_split_rejects(lib, kw, want):
+    assert _mt(lib, **kw) == want
+    assert lib.pa_last_error()
+    if kw.get("partition_size") == 100:
+        assert _mt_ws(lib, partition_size=100)[0] == B.PA_ERR_INVALID_ARG

@@ -39,15 +39,21 @@ class Mt:
         self.max_q = int(np.diff(b.query_start).max()) if b.num_seqs else 0
         self.out = torch.empty_like(self.q)
 
-    def run(self, seq_lens=None, block_tables=None, qs=None, max_q=None):
+    def run(self, seq_lens=None, block_tables=None, qs=None, max_q=None, partition_size=-1,
+            workspace=None):
         b = self.b
         say(f"pa_multi_token {b.name} seed={b.seed} {b.dtype} S={b.num_seqs} T={self.q.shape[0]} "
-            f"Hq={b.num_q_heads} Hkv={b.num_kv_heads} D={b.head_dim} bs={b.block_size}")
-        pa.pa_multi_token(self.q, self.k_cache, self.v_cache,
-                          self.block_tables if block_tables is None else block_tables,
-                          self.seq_lens if seq_lens is None else seq_lens,
-                          self.qs if qs is None else qs, b.block_size, b.num_kv_heads, b.scale,
-                          self.out, max_query_len=self.max_q if max_q is None else max_q)
+            f"Hq={b.num_q_heads} Hkv={b.num_kv_heads} D={b.head_dim} bs={b.block_size} "
+            f"partition_size={partition_size}")
+        call = pa.PreparedMultiToken(self.q, self.k_cache, self.v_cache,
+                                     self.block_tables if block_tables is None else block_tables,
+                                     self.seq_lens if seq_lens is None else seq_lens,
+                                     self.qs if qs is None else qs, b.block_size, b.num_kv_heads,
+                                     b.scale, self.out,
+                                     max_query_len=self.max_q if max_q is None else max_q,
+                                     partition_size=partition_size, workspace=workspace)
+        self.workspace_bytes = call.workspace_bytes
+        call()
         torch.cuda.synchronize()
         return self.out.double().cpu().numpy()
 
@@ -156,3 +162,94 @@ def test_contract_violations():
     got = g.run(qs=torch.from_numpy(bad_qs).cuda())
     assert (got[qs[2]:] == 7.0).all()
     check_close(got[:qs[2]], ref[:qs[2]], "bf16", "multi_token before the skipped ones")
+
+
+# ---- context split: partitions of the positions, merged with log-sum-exp weights
+
+@pytest.mark.parametrize("psz", [32, 64, 96, 128])
+@pytest.mark.parametrize("dtype,D,bs", [("bf16", 128, 16), ("f32", 64, 4), ("f16", 128, 32)])
+def test_split_parity(psz, dtype, D, bs):
+    """Forced partitions, including ones that start past some rows' causal limits and
+    partitions with nothing to do, against the oracle and against the unsplit call."""
+    b = inputs.make_batch("gqa_bf16", seed=11, dtype=dtype, head_dim=D, block_size=bs,
+                          num_seqs=len(LENS), lens=("fixed", LENS), new_tokens=NEW,
+                          max_blocks_per_seq=(max(LENS) + bs - 1) // bs + 2, cache_write=False)
+    g = Mt(b)
+    whole = g.run().copy()
+    got = g.run(partition_size=psz)
+    assert g.workspace_bytes > 0
+    ref = _oracle(b)
+    check_close(got, ref, dtype, f"split {psz} {dtype} D={D} bs={bs}")
+    check_close(got, whole, dtype, f"split {psz} vs unsplit")
+
+
+@pytest.mark.parametrize("psz", [64, 256])
+def test_split_long_chunks(psz):
+    """300-token chunks on up to 1200 cached tokens cut into partitions: row tiles whose
+    rows see different numbers of partitions, partitions wholly past some rows."""
+    lens = [300, 700, 1500, 333]
+    new = [300, 300, 300, 33]
+    b = inputs.make_batch("gqa_bf16", seed=12, num_seqs=4, lens=("fixed", lens), new_tokens=new,
+                          max_blocks_per_seq=100, cache_write=False, q_gain=4.0)
+    check_close(Mt(b).run(partition_size=psz), _oracle(b), "bf16", f"split long chunks {psz}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_split_automatic_verify(dtype):
+    """Draft-token verification: 2 sequences of 9-20 thousand cached tokens, 4 new ones
+    each, GQA-8.  Too few row tiles to fill the device, so the call splits by itself."""
+    b = inputs.make_batch("gqa_bf16", seed=13, dtype=dtype, num_seqs=2,
+                          lens=("fixed", [20000, 9001]), new_tokens=[4, 3],
+                          max_blocks_per_seq=1280, cache_write=False)
+    g = Mt(b)
+    got = g.run(partition_size=0)
+    assert g.workspace_bytes > 0
+    check_close(got, _oracle(b), dtype, f"automatic split verify {dtype}")
+
+
+def test_split_contract_violations():
+    """Under a split: bad lengths give NaN rows (written by the merge), a bad table
+    entry in any partition NaN rows for that sequence, skipped sequences nothing."""
+    lens, new = [40, 50, 60, 30], [8, 8, 8, 6]
+    b = inputs.make_batch("gqa_bf16", seed=7, num_seqs=4, lens=("fixed", lens), new_tokens=new,
+                          max_blocks_per_seq=5, cache_write=False)
+    ref = _oracle(b)
+    g = Mt(b)
+    sl = b.seq_lens.copy()
+    sl[0] = 5
+    sl[1] = 5 * 16 + 1
+    bt = b.block_tables.copy()
+    bt[2, 3] = b.num_blocks + 7     # in the second partition of 32 positions
+    g.out.fill_(7.0)
+    got = g.run(seq_lens=torch.from_numpy(sl).cuda(), block_tables=torch.from_numpy(bt).cuda(),
+                partition_size=32)
+    qs = b.query_start
+    for s in (0, 1, 2):
+        assert np.isnan(got[qs[s]:qs[s + 1]]).all(), s
+    check_close(got[qs[3]:], ref[qs[3]:], "bf16", "split healthy sequence")
+    bad_qs = b.query_start.copy()
+    bad_qs[3] = 9999
+    g.out.fill_(7.0)
+    got = g.run(qs=torch.from_numpy(bad_qs).cuda(), partition_size=32)
+    assert (got[qs[2]:] == 7.0).all()
+    check_close(got[:qs[2]], ref[:qs[2]], "bf16", "split before the skipped ones")
+
+
+def test_split_repeat_and_placement_are_bit_exact():
+    lens, new = [700, 2000, 450], [7, 64, 20]
+    b = inputs.make_batch("gqa_bf16", seed=14, num_seqs=3, lens=("fixed", lens), new_tokens=new,
+                          max_blocks_per_seq=130, cache_write=False)
+    g = Mt(b)
+    ws = torch.empty(1 << 27, dtype=torch.uint8, device="cuda:0")
+    first = g.run(partition_size=128, workspace=ws).copy()
+    assert 0 < g.workspace_bytes <= ws.numel()
+    ws.fill_(0xFF)                  # scratch: its old contents do not matter
+    np.testing.assert_array_equal(g.run(partition_size=128, workspace=ws), first)
+    N = b.num_blocks
+    perm = np.random.default_rng(2).permutation(N)
+    kc, vc = np.empty_like(b.k_cache), np.empty_like(b.v_cache)
+    kc[perm] = b.k_cache
+    vc[perm] = b.v_cache
+    bt = np.where(b.block_tables >= 0, perm[np.maximum(b.block_tables, 0)], -1).astype(np.int32)
+    b2 = inputs.Batch(**{**b.__dict__, "k_cache": kc, "v_cache": vc, "block_tables": bt})
+    np.testing.assert_array_equal(Mt(b2).run(partition_size=128, workspace=ws), first)
