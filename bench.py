@@ -17,7 +17,8 @@ Reported (one JSON line on stdout):
   cpu_baseline  the fp64 oracle on the host cores, on the same batch
   parity     GPU output of the last timed step against the oracle
   also       the same decode-only measurement for the long-context batches, and the
-             chunked-prefill batch through pa_multi_token (flops against the MFMA peak)
+             chunked-prefill and draft-verification batches through pa_multi_token
+             (against the roof each meets first: MFMA flops or HBM bytes)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -56,6 +57,9 @@ WORKLOAD_TEXT = {
     "prefill_bf16": "bf16 chunked prefill (pa_multi_token): 8 seqs, a 512-token chunk each on "
                     "1024-8192 cached tokens, causal, 64 q / 8 KV heads, head_dim 128, "
                     "block_size 16",
+    "verify_bf16": "bf16 draft-token verification (pa_multi_token, context split): 8 seqs, "
+                   "5 new tokens each on 8192-32768 cached tokens, causal, 64 q / 8 KV heads, "
+                   "head_dim 128, block_size 16",
 }
 
 
@@ -276,7 +280,7 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="minimum rotated copies of a batch")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--also", default="long_bf16_bs16,long_bf16_bs32,prefill_bf16",
+    ap.add_argument("--also", default="long_bf16_bs16,long_bf16_bs32,prefill_bf16,verify_bf16",
                     help="comma-separated secondary batches measured decode-only ('' for none)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 256 MiB device-to-device copy, a dispatch of known size "
@@ -329,15 +333,24 @@ def main():
         if rb.query_start is not None:
             fl = multi_token_flops(rb)
             tf = fl / (r["decode_ms"] * 1e-3) / 1e12
+            # the bound is the roof the call meets first: matrix cores when its flops per
+            # algorithmic byte exceed the machine's balance point, HBM otherwise
+            if fl / r["decode_bytes"] > PEAK_TFLOPS[rb.dtype] * 1e12 / (PEAK_GBPS * 1e9):
+                roof = {"bound": "mfma", "achieved": tf, "peak": PEAK_TFLOPS[rb.dtype],
+                        "unit": "TFLOP/s", "frac": tf / PEAK_TFLOPS[rb.dtype]}
+            else:
+                roof = {"bound": "hbm", "achieved": r["gbps"], "peak": PEAK_GBPS,
+                        "unit": "GB/s", "frac": r["gbps"] / PEAK_GBPS}
             also[name] = dict(workload=WORKLOAD_TEXT.get(name, name),
                               new_tokens=int(rb.query_start[-1]), sum_L=rb.total_tokens(),
                               call_us=r["decode_ms"] * 1e3, call_us_p10=r["decode_ms_p10"] * 1e3,
                               call_us_p90=r["decode_ms_p90"] * 1e3, algorithmic_flops=fl,
-                              roofline={"bound": "mfma", "achieved": tf,
-                                        "peak": PEAK_TFLOPS[rb.dtype], "unit": "TFLOP/s",
-                                        "frac": tf / PEAK_TFLOPS[rb.dtype]},
-                              algorithmic_bytes=r["decode_bytes"], achieved_gbps=r["gbps"])
-            log(f"{name}: {tf:.0f} TFLOP/s = {tf / PEAK_TFLOPS[rb.dtype]:.1%} of dense MFMA peak")
+                              roofline=roof, algorithmic_bytes=r["decode_bytes"],
+                              achieved_gbps=r["gbps"],
+                              split_workspace_bytes=r["copies"][0].decode.workspace_bytes)
+            log(f"{name}: {tf:.0f} TFLOP/s = {tf / PEAK_TFLOPS[rb.dtype]:.1%} of dense MFMA peak; "
+                f"{r['gbps']:.0f} GB/s = {r['gbps'] / PEAK_GBPS:.1%} of HBM peak "
+                f"(bound: {roof['bound']})")
             del r
             torch.cuda.empty_cache()
             continue

@@ -15,23 +15,26 @@
 // which is where the matrix cores pay.
 //
 // Work.  A workgroup (4 waves) owns 128 consecutive rows of one (sequence, KV head):
-// row r is new token r / G, query head r % G of the group.  Each wave holds 32 rows as
-// two 16-row MFMA tiles.  The workgroup walks the sequence's tokens in 32-token chunks
-// up to the last position its rows may see; each chunk's K and V are gathered through
-// the block table once into LDS (double-buffered, the next chunk's loads in flight while
-// the current one is computed) and read there by all four waves.
+// row r is new token r / G, query head r % G of the group.  Each wave holds two 16-row
+// MFMA tiles, tiles w and w + 4 of the workgroup's eight, so that a workgroup with few
+// rows still spreads them over its waves; tiles without rows are skipped.  The
+// workgroup walks the sequence's tokens in 32-token chunks up to the last position its
+// rows may see; each chunk's K and V are gathered through the block table once, by
+// global -> LDS loads with no register staging, into one of four LDS buffers (three
+// chunks in flight while one is computed; two buffers for fp32 at head size 128), and
+// read there by all four waves.
 //
 // MFMA layouts (as in the decode kernel, rows of the problem on the N side):
 //   logits^T = K (32 tokens x D) . Q^T (D x 16 rows), two 16-token tiles per chunk
 //   taking tokens {8i..8i+3} and {8i+4..8i+7}, so lane (row c, quad i) ends up holding
 //   tokens 8i..8i+7 of row c: exactly the B operand (P^T) of
 //   O^T += V^T (16 dims x 32 tokens) . P^T (32 tokens x 16 rows).
-// K is stored in LDS in that MFMA row order ([tile][row][D], padded), V dimension-major
-// ([D][32 tokens], padded), so every operand is one 16-byte LDS read per lane.
+// K is stored in LDS in that MFMA row order, V segment-major (see Shape), so every
+// operand is one 16-byte LDS read per lane, free of bank conflicts.
 //
 // Masking.  Positions past the causal limit of a row are removed by select (-inf
-// before the max, weight 0).  Positions at or past L may hold anything, so they are
-// written to LDS as zeros and never multiplied.
+// before the max, weight 0).  Positions at or past L may hold anything: their logits are
+// masked, and their values are cleared in LDS before the weighted sum.
 //
 // Precision.  Products accumulate in fp32.  The softmax weights enter the second product
 // as a hi + lo pair for bf16 (its 8 significant bits alone would show next to the
@@ -44,8 +47,8 @@
 // workgroup leaves its rows' running maximum, sum and unnormalised output in a
 // workspace, and a second launch combines them with log-sum-exp weights.
 //
-// Launch.  One workgroup per (row tile, partition, KV head, sequence).  Workgroups are dispatched
-// to the eight XCDs in turn; the numbering deals whole (sequence, KV head) groups to
+// Launch.  One workgroup per (row tile, partition, KV head, sequence).  Workgroups are
+// dispatched to the eight XCDs in turn; the numbering deals whole (sequence, KV head) groups to
 // the XCDs round-robin, so that the row tiles of a group share their XCD's L2 copy of
 // the K/V they all read, and every XCD gets a share of every sequence.
 #include <math.h>
@@ -158,34 +161,88 @@ __device__ __forceinline__ void store4(T* p, f32x4 v) {
   }
 }
 
+// LDS layout of one chunk (no padding; the bank spread comes from the layouts):
+//   keys    [32 rows][KSEG segments of 16 bytes], rows in MFMA order, and segment j of
+//           row r stored at position j ^ kswz(r): the 16 rows one MFMA operand read
+//           touches then fall on 16 different 16-byte bank groups
+//   values  [CH / TPS segments][D dimensions][TPS tokens]: a value operand read (one
+//           segment, 16 consecutive dimensions) covers 256 consecutive bytes
+// Both are filled by global -> LDS loads that put lane l's bytes at base + l * size;
+// each lane picks the global address whose bytes belong at its slot.
 template <typename T, int D, int BS>
 struct Shape {
   static constexpr int E = sizeof(T);
   static constexpr int EPL = 16 / E;                 // elements per 16 bytes
   static constexpr int KL = D * E / 64;              // 16-byte operand reads per key row
   static constexpr int NT = D / 16;                  // 16-dimension output tiles
-  static constexpr int KROW = D + EPL;               // LDS pitch of a key row (elements)
-  static constexpr int VROW = CH + EPL;              // LDS pitch of a value row
-  static constexpr int KSEG = D * E / 16;            // 16-byte pieces of a key row
-  static constexpr int KP = CH * KSEG / THREADS;     // key pieces per thread per chunk
-  static constexpr int VPE = EPL < BS ? EPL : BS;    // tokens per value piece
-  static constexpr int VSEG = CH / VPE;              // value pieces per dimension
-  static constexpr int VP = D * VSEG / THREADS;      // value pieces per thread per chunk
-  static_assert(KP >= 1 && VP >= 1, "chunk pieces must cover the workgroup");
-  typedef typename std::conditional<VPE * E == 16, u32x4, u32x2>::type VPiece;
+  static constexpr int KSEG = D * E / 16;            // 16-byte segments of a key row
+  static constexpr int KI = CH * KSEG / 64 / WAVES;  // key loads per wave per chunk
+  // the rows under one key load (64 / KSEG of them) are one run of 4 consecutive
+  // tokens, except at KSEG = 8: two runs 8 tokens apart, in two blocks when BS <= 8
+  static constexpr int NBK = (KSEG == 8 && BS <= 8) ? 2 : 1;
+  static constexpr int TPS = 16 / E;                 // tokens per value segment
+  static constexpr int VB = TPS <= BS ? 16 : 4;      // bytes per lane of a value load
+  static constexpr int VI = CH * D * E / (64 * VB) / WAVES;  // value loads per wave per chunk
+  static constexpr int NBV = VB == 16 ? 1 : 2;       // blocks under one value load
+  static constexpr int CHUNK = CH * D;               // elements of K (and of V) per chunk
+  static constexpr int NBUF = 2 * CHUNK * E <= 16384 ? 4 : 2;  // chunk buffers in LDS
+  static constexpr int LOADS = KI + VI;              // loads per wave per chunk
+  static_assert(KI >= 1 && VI >= 1, "chunk loads must cover the workgroup");
+  static_assert(KSEG == 8 || KSEG == 16 || KSEG == 32, "key rows of 128, 256 or 512 bytes");
+  static_assert(D % 64 == 0, "a value load covers one segment of 64 dimensions or more");
 };
 
 // rows of the LDS key tile are in MFMA order: token t = 8a + 4q + b sits at 16q + 4a + b
-__device__ __forceinline__ int krow_of(int t) { return 16 * ((t >> 2) & 1) + 4 * (t >> 3) + (t & 3); }
+__device__ __forceinline__ constexpr int krow_of(int t) {
+  return 16 * ((t >> 2) & 1) + 4 * (t >> 3) + (t & 3);
+}
+__device__ __forceinline__ constexpr int tok_of_krow(int r) {
+  return 8 * ((r >> 2) & 3) + 4 * (r >> 4) + (r & 3);
+}
+// segment swizzle of key row r: a different 16-byte bank group for each of 16 rows
+template <int KSEG>
+__device__ __forceinline__ constexpr int kswz(int r) {
+  return KSEG >= 16 ? (r & 15) : ((r >> 1) & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One global -> LDS load: lane l's SIZE bytes at g land at lds + l * SIZE.  Issued as
+// inline assembly so that the compiler's wait insertion, which cannot tell the chunk
+// buffers apart, does not wait for every load in flight before each LDS read; the waits
+// for these loads are the pipeline's own (wait_loads_and_sync).
+template <int SIZE>
+__device__ __forceinline__ void load_to_lds(const void* g, const void* lds) {
+  const uint32_t m = (uint32_t)(uintptr_t)(lds_void*)lds;
+  if constexpr (SIZE == 16) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 ::"s"(m), "v"(g) : "memory", "m0");
+  } else {
+    static_assert(SIZE == 4, "16- or 4-byte loads");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 ::"s"(m), "v"(g) : "memory", "m0");
+  }
+}
+
+// Waits of the chunk pipeline.  The loads into LDS are counted by vmcnt; a wave waits
+// until at most N of its own are outstanding, then the workgroup barrier makes every
+// wave's data visible.  The barrier is issued directly (not through a release fence,
+// which would also wait for the chunks still in flight); the LDS reads before it have
+// returned (lgkmcnt(0)), so nothing of the buffer about to be refilled is still read.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_sync() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <typename T, int D, int BS>
 __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_kernel(MultiTokenParams P) {
   typedef Shape<T, D, BS> SH;
-  constexpr int KL = SH::KL, NT = SH::NT, EPL = SH::EPL;
-  typedef typename SH::VPiece VPiece;
+  constexpr int KL = SH::KL, NT = SH::NT, EPL = SH::EPL, KSEG = SH::KSEG, TPS = SH::TPS;
+  constexpr int NBUF = SH::NBUF;
 
-  __shared__ __attribute__((aligned(16))) T sk[2][CH * SH::KROW];
-  __shared__ __attribute__((aligned(16))) T sv[2][D * SH::VROW];
+  __shared__ __attribute__((aligned(16))) T sk[NBUF][SH::CHUNK];
+  __shared__ __attribute__((aligned(16))) T sv[NBUF][SH::CHUNK];
 
   // ---- which (row tile, context partition, KV head, sequence): (sequence, KV head)
   // groups are dealt to the XCDs in turn, and every row tile and partition of a group
@@ -248,108 +305,102 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
   // largest logit is the largest raw dot product.
   const float sc = fabsf(P.scale_log2);
   const uint32_t qsign = P.scale_log2 < 0.f ? (sizeof(T) == 2 ? 0x80008000u : 0x80000000u) : 0u;
+  // Row tile t of wave w holds rows 16 (w + 4t) .. 16 (w + 4t) + 15 of the workgroup's
+  // 128, so that a workgroup with few rows (a few new tokens) spreads them over its
+  // waves; a tile with no row of the problem is skipped (nlive: live tiles of the wave).
+  const int nlive = (R0 + 16 * wave < rend) + (R0 + 16 * (wave + WAVES) < rend);
   u32x4 qf[NTILE][KL];
   int lim[NTILE];
   bool rvalid[NTILE];
   int64_t orow[NTILE];
 #pragma unroll
   for (int t = 0; t < NTILE; ++t) {
-    const int rr = R0 + wave * (NTILE * 16) + t * 16 + col;
+    const int rr = R0 + 16 * (wave + WAVES * t) + col;
     rvalid[t] = rr < rend;
     const int rc = min(rr, rend - 1);
     const int j = rc / G;
     lim[t] = ctx + j;
     orow[t] = (int64_t)(q0 + j) * Hq + g * G + rc % G;
     const T* qp = (const T*)P.q + orow[t] * D + quad * EPL;
+    // a row past the tile repeats the tile's last row (so every load is in bounds and
+    // they all go out together); its results are never stored
 #pragma unroll
-    for (int c = 0; c < KL; ++c)
-      qf[t][c] = rvalid[t] ? (*reinterpret_cast<const u32x4*>(qp + c * 4 * EPL) ^ qsign)
-                           : u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < KL; ++c) qf[t][c] = *reinterpret_cast<const u32x4*>(qp + c * 4 * EPL) ^ qsign;
   }
 
-  // ---- chunk loading, block ids one chunk ahead of the data.  Key piece p (of a
-  // thread's KP) is token p / KSEG of the chunk, 16-byte segment p % KSEG of its row;
-  // value piece p is dimension p % D, tokens VPE * (p / D) onwards.  One wave-wide load
-  // instruction thus covers whole token groups, and the physical block it reads is the
-  // same for all its lanes: one scalar table read per instruction, and the block's
-  // address is formed in scalar registers.  Only 8-token key groups at block size 4
-  // span two blocks; there each lane picks one of the two.
-  constexpr int TPI = 64 / SH::KSEG;              // tokens under one wave-wide key load
-  constexpr int NBK = TPI > BS ? TPI / BS : 1;    // blocks those tokens span
-  static_assert(NBK <= 2, "a key load spans at most two blocks");
+  // ---- chunk loading, global -> LDS.  Key load i of a wave fills 64 consecutive key
+  // slots (16 bytes each), value load i 64 consecutive value slots (VB bytes each); the
+  // tokens under one load lie in at most two blocks, whose ids are scalar table reads.
+  // The lane's offset inside its block is the same for every chunk (chunks start on
+  // block edges), so it is computed once.
   const int32_t AS4* tbls = (const int32_t AS4*)tbl;
   int bad = 0;
-  int kid[SH::KP][NBK], vid[SH::VP];
-  u32x4 kr[SH::KP];
-  VPiece vr[SH::VP];
-  // table reads go out one chunk before their ids are used, and are checked only then,
-  // so that the wait for them falls long after they arrived
+  int koff[SH::KI], voff[SH::VI];
+  int kjr[SH::KI][SH::NBK], vjr[SH::VI][SH::NBV];  // blocks (within the chunk), uniform
+#pragma unroll
+  for (int i = 0; i < SH::KI; ++i) {
+    const int I = wave + WAVES * i;
+    const int p = 64 * I + lane;
+    const int r = p / KSEG;
+    const int t = tok_of_krow(r);
+    koff[i] = (t % BS) * D + ((p % KSEG) ^ kswz<KSEG>(r)) * EPL;
+#pragma unroll
+    for (int u = 0; u < SH::NBK; ++u) kjr[i][u] = tok_of_krow(64 * I / KSEG + 4 * u) / BS;
+  }
+#pragma unroll
+  for (int i = 0; i < SH::VI; ++i) {
+    const int I = wave + WAVES * i;
+    if constexpr (SH::VB == 16) {  // slot p: segment p / D, dimension p % D
+      const int p = 64 * I + lane;
+      voff[i] = (p % D) * BS + ((p / D) * TPS) % BS;
+      vjr[i][0] = ((64 * I / D) * TPS) / BS;
+    } else {  // 4-byte slots at block size 4: tokens 8s + 2w, 8s + 2w + 1 of segment s
+      const int q = 64 * I + lane;
+      const int w = q % 4;
+      voff[i] = ((q / 4) % D) * BS + 2 * (w & 1);
+#pragma unroll
+      for (int u = 0; u < SH::NBV; ++u) vjr[i][u] = 2 * ((16 * I) / D) + u;
+    }
+  }
   auto block_id = [&](int j) { return tbls[min(j, last_blk)]; };
   auto checked = [&](int id) {  // ids outside the pool -> 0, and the workgroup's rows NaN
     const bool ok = (uint32_t)id < nblk32;
     bad |= !ok;
     return ok ? id : 0;
   };
-  auto load_ids = [&](int c, int (&ki)[SH::KP][NBK], int (&vi)[SH::VP]) {
-    const int t0 = c * CH;
+  // table reads go out one chunk before their ids are used, and are checked only then
+  int kid[SH::KI][SH::NBK], vid[SH::VI][SH::NBV];
+  auto load_ids = [&](int c) {
+    const int j0 = c * (CH / BS);
 #pragma unroll
-    for (int i = 0; i < SH::KP; ++i) {
-      const int j = (t0 + (64 * wave + THREADS * i) / SH::KSEG) / BS;
+    for (int i = 0; i < SH::KI; ++i)
 #pragma unroll
-      for (int u = 0; u < NBK; ++u) ki[i][u] = block_id(j + u);
-    }
+      for (int u = 0; u < SH::NBK; ++u) kid[i][u] = block_id(j0 + kjr[i][u]);
 #pragma unroll
-    for (int i = 0; i < SH::VP; ++i)
-      vi[i] = block_id((t0 + ((64 * wave + THREADS * i) / D) * SH::VPE) / BS);
+    for (int i = 0; i < SH::VI; ++i)
+#pragma unroll
+      for (int u = 0; u < SH::NBV; ++u) vid[i][u] = block_id(j0 + vjr[i][u]);
   };
-  auto load_data = [&]() {
+  auto issue = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < SH::KP; ++i) {
-      const int p = tid + THREADS * i;
-      const int t = p / SH::KSEG;  // (t0 + t) % BS == t % BS: chunks start on block edges
+    for (int i = 0; i < SH::KI; ++i) {
       int id = checked(kid[i][0]);
-      if constexpr (NBK == 2) {
+      if constexpr (SH::NBK == 2) {
         const int id1 = checked(kid[i][1]);
-        id = ((t % TPI) >= BS) ? id1 : id;
+        id = lane >= 32 ? id1 : id;
       }
-      const T* blk = kbase + (int64_t)id * blk_stride;
-      kr[i] = *reinterpret_cast<const u32x4*>(blk + (t % BS) * D + (p % SH::KSEG) * EPL);
+      load_to_lds<16>(kbase + (int64_t)id * blk_stride + koff[i],
+                      &sk[buf][64 * (wave + WAVES * i) * EPL]);
     }
 #pragma unroll
-    for (int i = 0; i < SH::VP; ++i) {
-      const int p = tid + THREADS * i;
-      const int tk = (p / D) * SH::VPE;
-      const T* blk = vbase + (int64_t)checked(vid[i]) * blk_stride;
-      vr[i] = *reinterpret_cast<const VPiece*>(blk + (p % D) * BS + tk % BS);
-    }
-  };
-  auto store_lds = [&](int c, int buf) {
-    const int t0 = c * CH;
-#pragma unroll
-    for (int i = 0; i < SH::KP; ++i) {
-      const int p = tid + THREADS * i;
-      const int t = p / SH::KSEG;
-      const u32x4 v = (t0 + t < L) ? kr[i] : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&sk[buf][krow_of(t) * SH::KROW + (p % SH::KSEG) * EPL]) = v;
-    }
-#pragma unroll
-    for (int i = 0; i < SH::VP; ++i) {
-      const int p = tid + THREADS * i;
-      const int tk = (p / D) * SH::VPE;
-      VPiece v = vr[i];
-      if (t0 + tk + SH::VPE > L) {  // values at or past L may be NaN: zero them
-        constexpr int W = sizeof(VPiece) / 4;
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-          if constexpr (sizeof(T) == 2) {
-            const int e = t0 + tk + 2 * w;
-            v[w] &= (e < L ? 0x0000FFFFu : 0u) | (e + 1 < L ? 0xFFFF0000u : 0u);
-          } else {
-            v[w] = (t0 + tk + w < L) ? v[w] : 0u;
-          }
-        }
+    for (int i = 0; i < SH::VI; ++i) {
+      int id = checked(vid[i][0]);
+      if constexpr (SH::NBV == 2) {
+        const int id1 = checked(vid[i][1]);
+        id = (lane & 2) ? id1 : id;
       }
-      *reinterpret_cast<VPiece*>(&sv[buf][(p % D) * SH::VROW + tk]) = v;
+      load_to_lds<SH::VB>(vbase + (int64_t)id * blk_stride + voff[i],
+                          &sv[buf][64 * (wave + WAVES * i) * SH::VB / SH::E]);
     }
   };
 
@@ -367,20 +418,24 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
   // tile the softmax and the weighted sum.  Only a chunk that crosses the causal limit of
   // some row of the workgroup is masked.
   auto compute = [&](int c, int buf) {
+    if (nlive == 0) return;
     const int t0 = c * CH;
     const bool masked = t0 + CH - 1 > lim_lo;  // uniform
     // logits^T tiles a (tokens 8i..8i+3) and b (8i+4..8i+7); A read once for both row tiles
     f32x4 sa[NTILE], sb[NTILE];
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) sa[t] = sb[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const T* ka = &sk[buf][col * SH::KROW + quad * EPL];
-    const T* kb = &sk[buf][(16 + col) * SH::KROW + quad * EPL];
+    // key rows col (tile a) and 16 + col (tile b) share their swizzle
+    const T* ka = &sk[buf][col * KSEG * EPL];
+    const T* kb = ka + 16 * KSEG * EPL;
 #pragma unroll
     for (int k = 0; k < KL; ++k) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(ka + k * 4 * EPL);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(kb + k * 4 * EPL);
+      const int seg = (4 * k + quad) ^ kswz<KSEG>(col);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(ka + seg * EPL);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(kb + seg * EPL);
 #pragma unroll
       for (int t = 0; t < NTILE; ++t) {
+        if (t >= nlive) break;
         if constexpr (sizeof(T) == 2) {
           typedef typename V8<T>::type VT;
           sa[t] = mma16(__builtin_bit_cast(VT, a), __builtin_bit_cast(VT, qf[t][k]), sa[t]);
@@ -398,9 +453,11 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
     }
     // per row tile: softmax of the chunk, then its weighted sum
     const int tfirst = t0 + 8 * quad;
-    const T* vrow = &sv[buf][col * SH::VROW + 8 * quad];  // dimension 16nn + col, tokens 8quad..
+    // dimension 16nn + col, tokens 8quad .. 8quad + 7: value segment quad (two for fp32)
+    const T* vrow = &sv[buf][(8 / TPS) * quad * D * TPS + col * TPS];
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
+      if (t >= nlive) break;
       float z[8];  // raw dot products; the scale is applied inside the exponent
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -445,7 +502,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
         split_weights<T>(pr, phi, plo);
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn) {
-          const VT vv = *reinterpret_cast<const VT*>(vrow + 16 * nn * SH::VROW);
+          const VT vv = *reinterpret_cast<const VT*>(vrow + 16 * nn * TPS);
           acc[t][nn] = mma16(vv, __builtin_bit_cast(VT, phi), acc[t][nn]);
           if constexpr (std::is_same<T, __bf16>::value)
             acc[t][nn] = mma16(vv, __builtin_bit_cast(VT, plo), acc[t][nn]);
@@ -453,8 +510,8 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
       } else {
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn) {
-          const f32x4 lo = *reinterpret_cast<const f32x4*>(vrow + 16 * nn * SH::VROW);
-          const f32x4 hi = *reinterpret_cast<const f32x4*>(vrow + 16 * nn * SH::VROW + 4);
+          const f32x4 lo = *reinterpret_cast<const f32x4*>(vrow + 16 * nn * TPS);
+          const f32x4 hi = *reinterpret_cast<const f32x4*>(vrow + 16 * nn * TPS + D * TPS);
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[t][nn] = mma4(lo[e], pr[e], acc[t][nn]);
 #pragma unroll
@@ -464,28 +521,47 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
     }
   };
 
-  // ---- the chunk pipeline over chunks c_lo .. nch-1
-  load_ids(c_lo, kid, vid);
-  load_data();
-  store_lds(c_lo, c_lo & 1);
-  if (c_lo + 1 < nch) load_ids(c_lo + 1, kid, vid);
-  __syncthreads();
-  for (int c = c_lo; c < nch; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < nch) load_data();
-    int kid2[SH::KP][NBK], vid2[SH::VP];
-    if (c + 2 < nch) load_ids(c + 2, kid2, vid2);
-    compute(c, buf);
-    if (c + 1 < nch) store_lds(c + 1, buf ^ 1);
-    if (c + 2 < nch) {
+  // ---- the chunk pipeline over chunks c_lo .. nch-1: NBUF - 1 chunks in flight
+  // ahead of the one computed.  Positions at or past L may hold anything: values there
+  // are cleared in LDS before use (their weights are 0, but 0 * NaN is not); keys there
+  // only reach logits that are masked by select.
+  // the query fragments arrive before the first chunk loads go out (the compiler, not
+  // seeing those loads, would otherwise wait for all of them at the first use of Q)
 #pragma unroll
-      for (int i = 0; i < SH::KP; ++i)
+  for (int t = 0; t < NTILE; ++t)
 #pragma unroll
-        for (int u = 0; u < NBK; ++u) kid[i][u] = kid2[i][u];
+    for (int c = 0; c < KL; ++c) asm volatile("" ::"v"(qf[t][c]));
+  load_ids(c_lo);
 #pragma unroll
-      for (int i = 0; i < SH::VP; ++i) vid[i] = vid2[i];
+  for (int j = 0; j < NBUF - 1; ++j) {
+    if (c_lo + j < nch) {
+      issue((c_lo + j) & (NBUF - 1));
+      if (c_lo + j + 1 < nch) load_ids(c_lo + j + 1);
     }
-    __syncthreads();
+  }
+  for (int c = c_lo; c < nch; ++c) {
+    const int buf = c & (NBUF - 1);
+    const int ahead = min(NBUF - 2, nch - 1 - c);  // chunks issued after this one
+    if constexpr (NBUF == 4) {
+      if (ahead >= 2) wait_loads_and_sync<2 * SH::LOADS>();
+      else if (ahead == 1) wait_loads_and_sync<SH::LOADS>();
+      else wait_loads_and_sync<0>();
+    } else {
+      wait_loads_and_sync<0>();
+    }
+    const int t0 = c * CH;
+    if (t0 + CH > L) {
+      for (int i = tid; i < (t0 + CH - L) * D; i += THREADS) {
+        const int tok = L - t0 + i / D;
+        sv[buf][((tok / TPS) * D + i % D) * TPS + tok % TPS] = (T)0.f;
+      }
+      lds_sync();
+    }
+    if (c + NBUF - 1 < nch) {
+      issue((c + NBUF - 1) & (NBUF - 1));  // the buffer computed last iteration
+      if (c + NBUF < nch) load_ids(c + NBUF);
+    }
+    compute(c, buf);
   }
   bad = __syncthreads_or(bad);
 
@@ -499,7 +575,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
     for (int t = 0; t < NTILE; ++t) {
       const float l = sum_over_quads(l_run[t]);
       if (!rvalid[t]) continue;
-      const int64_t r = tile0 + wave * (NTILE * 16) + t * 16 + col;
+      const int64_t r = tile0 + 16 * (wave + WAVES * t) + col;
       float* po = P.part_o + r * D + 4 * quad;
 #pragma unroll
       for (int nn = 0; nn < NT; ++nn)
@@ -525,15 +601,25 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
   }
 }
 
-// The merge after a split launch: one workgroup per (row tile, KV head, sequence)
-// combines each row's partitions with log-sum-exp weights, in partition order, and
-// writes the output row (NaN rows for a length the table cannot hold).  Partitions that
-// start past the tile's last causal limit were skipped by the main kernel; the first
-// partition always holds position 0, which every row sees.
+// The merge after a split launch.  A workgroup combines MROWS rows of one (row tile,
+// KV head, sequence), one thread per (row, 4 dimensions), over the row's partitions
+// with log-sum-exp weights in partition order, and writes the output rows (NaN rows for
+// a length the table cannot hold).  Partitions that start past the tile's last causal
+// limit were skipped by the main kernel and are not read; the first partition always
+// holds position 0, which every row sees.
+template <int D>
+struct Merge {
+  static constexpr int MROWS = THREADS / (D / 4);  // rows per workgroup
+};
+
 template <typename T, int D>
 __global__ __launch_bounds__(THREADS) void multi_token_merge_kernel(MultiTokenParams P) {
-  const int x = (int)(blockIdx.x % P.row_tiles);
-  const int group = (int)(blockIdx.x / P.row_tiles);
+  constexpr int MROWS = Merge<D>::MROWS;
+  const int slabs = (P.part_rows + MROWS - 1) / MROWS;
+  const int slab = (int)(blockIdx.x % slabs);
+  const int tile = (int)(blockIdx.x / slabs);
+  const int x = tile % P.row_tiles;
+  const int group = tile / P.row_tiles;
   const int g = group % P.num_kv_heads;
   const int s = group / P.num_kv_heads;
   const int G = P.group, Hq = P.num_q_heads;
@@ -542,39 +628,41 @@ __global__ __launch_bounds__(THREADS) void multi_token_merge_kernel(MultiTokenPa
   if (q0 < 0 || n < 0 || q1 > P.num_tokens) return;
   const int R0 = x * ROWS;
   const int rend = min(n * G, R0 + ROWS);
-  if (R0 >= rend) return;
+  const int r = slab * MROWS + (int)threadIdx.x / (D / 4);  // row within the tile
+  if (R0 + r >= rend) return;
+  const int d4 = ((int)threadIdx.x % (D / 4)) * 4;
+  const int rr = R0 + r;
+  T* o = (T*)P.out + ((int64_t)(q0 + rr / G) * Hq + g * G + rr % G) * D + d4;
+  const float nan = __builtin_nanf("");
   const int L = P.seq_lens[s];
-  const bool invalid = L > P.max_tokens || n > L;
+  if (L > P.max_tokens || n > L) {
+    store4(o, f32x4{nan, nan, nan, nan});
+    return;
+  }
   const int lim_hi = L - n + (rend - 1) / G;
   const int used = min(P.parts, (lim_hi / CH) / (P.part_tokens / CH) + 1);
-  const int64_t tile0 = (((int64_t)s * P.num_kv_heads + g) * P.row_tiles + x) * P.parts * P.part_rows;
-  const int64_t pstride = P.part_rows;
-  for (int it = threadIdx.x; it < (rend - R0) * (D / 4); it += THREADS) {
-    const int r = it / (D / 4);
-    const int d4 = (it - r * (D / 4)) * 4;
-    const int rr = R0 + r;
-    T* o = (T*)P.out + ((int64_t)(q0 + rr / G) * Hq + g * G + rr % G) * D + d4;
-    if (invalid) {
-      const float nan = __builtin_nanf("");
-      store4(o, f32x4{nan, nan, nan, nan});
-      continue;
-    }
-    float M = -INFINITY;
-    for (int p = 0; p < used; ++p) M = fmaxf(M, P.part_ml[2 * (tile0 + p * pstride + r)]);
-    float Ls = 0.f;
-    f32x4 O = {0.f, 0.f, 0.f, 0.f};
-    bool nan_seen = false;
-    for (int p = 0; p < used; ++p) {
-      const int64_t pr = tile0 + p * pstride + r;
-      const f32x2 ml = *reinterpret_cast<const f32x2*>(P.part_ml + 2 * pr);
-      nan_seen |= ml[0] != ml[0];
-      const float w = exp2_fast(ml[0] - M);  // 0 for a partition none of whose positions the row sees
-      Ls += w * ml[1];
-      O += w * *reinterpret_cast<const f32x4*>(P.part_o + pr * D + d4);
-    }
-    const float nan = __builtin_nanf("");
-    store4(o, nan_seen ? f32x4{nan, nan, nan, nan} : O / Ls);
+  const int64_t row0 = (((int64_t)s * P.num_kv_heads + g) * P.row_tiles + x) * P.parts * P.part_rows + r;
+  const float* ml = P.part_ml + 2 * row0;
+  const float* po = P.part_o + row0 * D + d4;
+  const int64_t ps = P.part_rows;  // rows between one partition and the next
+  float M = -INFINITY;
+  bool nan_seen = false;
+#pragma unroll 4
+  for (int p = 0; p < used; ++p) {
+    const float m = ml[2 * ps * p];
+    nan_seen |= m != m;
+    M = fmaxf(M, m);
   }
+  float Ls = 0.f;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int p = 0; p < used; ++p) {
+    const f32x2 v = *reinterpret_cast<const f32x2*>(ml + 2 * ps * p);
+    const float w = exp2_fast(v[0] - M);  // 0 for a partition none of whose positions the row sees
+    Ls += w * v[1];
+    O += w * *reinterpret_cast<const f32x4*>(po + ps * D * p);
+  }
+  store4(o, nan_seen ? f32x4{nan, nan, nan, nan} : O / Ls);
 }
 
 template <typename T, int D>
@@ -631,7 +719,9 @@ int multi_token_rows_per_group() { return ROWS; }
 hipError_t launch_multi_token_merge(int dtype, int head_dim, const MultiTokenParams& p,
                                     hipStream_t stream) {
   const void* k = multi_token_merge_for(dtype, head_dim);
-  const int64_t grid = (int64_t)p.row_tiles * p.num_kv_heads * p.num_seqs;
+  const int mrows = head_dim == 64 ? Merge<64>::MROWS : Merge<128>::MROWS;
+  const int64_t grid = (int64_t)p.row_tiles * p.num_kv_heads * p.num_seqs *
+                       ((p.part_rows + mrows - 1) / mrows);
   if (!k || grid <= 0 || grid > 0x7fffffff || p.parts < 2) return hipErrorInvalidValue;
   MultiTokenParams arg = p;
   void* args[] = {&arg};

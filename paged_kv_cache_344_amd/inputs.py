@@ -70,6 +70,13 @@ CONFIGS = {
                          head_dim=128, block_size=16, max_blocks_per_seq=544,
                          lens=("chunk", 1024, 8192, 512), pool=("slack", 0.10),
                          cache_write=False),
+    # draft-token verification (speculative decoding over the paged cache): 5 new tokens
+    # per sequence on 8192-32768 cached ones, GQA-8; too few row tiles to fill the
+    # device, so pa_multi_token splits the context
+    "verify_bf16": dict(dtype="bf16", num_seqs=8, num_q_heads=64, num_kv_heads=8,
+                        head_dim=128, block_size=16, max_blocks_per_seq=2049,
+                        lens=("chunk", 8192, 32768, 5), pool=("slack", 0.10),
+                        cache_write=False),
 }
 
 
