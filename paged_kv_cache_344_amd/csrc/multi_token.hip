@@ -603,7 +603,8 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
 
 // The merge after a split launch.  A workgroup combines MROWS rows of one (row tile,
 // KV head, sequence), one thread per (row, 4 dimensions), over the row's partitions
-// with log-sum-exp weights in partition order, and writes the output rows (NaN rows for
+// with log-sum-exp weights in partition order (a running maximum, as in the main
+// kernel's chunk loop), and writes the output rows (NaN rows for
 // a length the table cannot hold).  Partitions that start past the tile's last causal
 // limit were skipped by the main kernel and are not read; the first partition always
 // holds position 0, which every row sees.
@@ -645,22 +646,24 @@ __global__ __launch_bounds__(THREADS) void multi_token_merge_kernel(MultiTokenPa
   const float* ml = P.part_ml + 2 * row0;
   const float* po = P.part_o + row0 * D + d4;
   const int64_t ps = P.part_rows;  // rows between one partition and the next
-  float M = -INFINITY;
-  bool nan_seen = false;
-#pragma unroll 4
-  for (int p = 0; p < used; ++p) {
-    const float m = ml[2 * ps * p];
-    nan_seen |= m != m;
-    M = fmaxf(M, m);
-  }
-  float Ls = 0.f;
-  f32x4 O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int p = 0; p < used; ++p) {
-    const f32x2 v = *reinterpret_cast<const f32x2*>(ml + 2 * ps * p);
-    const float w = exp2_fast(v[0] - M);  // 0 for a partition none of whose positions the row sees
-    Ls += w * v[1];
-    O += w * *reinterpret_cast<const f32x4*>(po + ps * D * p);
+  // one pass in partition order with a running maximum: the loads of later partitions
+  // do not wait for the arithmetic of earlier ones.  Partition 0 holds position 0, so
+  // the maximum is finite from the first step on; a later partition none of whose
+  // positions the row sees has maximum -inf and weight exp2(-inf) = 0.
+  f32x2 v = *reinterpret_cast<const f32x2*>(ml);
+  float M = v[0], Ls = v[1];
+  f32x4 O = *reinterpret_cast<const f32x4*>(po);
+  bool nan_seen = M != M;
+#pragma unroll 8
+  for (int p = 1; p < used; ++p) {
+    v = *reinterpret_cast<const f32x2*>(ml + 2 * ps * p);
+    const f32x4 op = *reinterpret_cast<const f32x4*>(po + ps * D * p);
+    nan_seen |= v[0] != v[0];
+    const float Mn = fmaxf(M, v[0]);
+    const float a = exp2_fast(M - Mn), w = exp2_fast(v[0] - Mn);
+    Ls = Ls * a + v[1] * w;
+    O = O * a + op * w;
+    M = Mn;
   }
   store4(o, nan_seen ? f32x4{nan, nan, nan, nan} : O / Ls);
 }

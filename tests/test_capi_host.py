@@ -265,7 +265,7 @@ def _mt_expected(S, T, mq, Hq, Hkv, D, MB, bs, psz):
         return 0
     else:
         min_part = max(256, -(-16 * part_rows // 32) * 32)
-        parts = min(-(-512 // triples), max_tokens // min_part)
+        parts = min(-(-2048 // triples), max_tokens // min_part)
         if triples >= 512 or parts < 2:
             return 0
         pt = -(-(-(-max_tokens // parts)) // 32) * 32
@@ -301,9 +301,10 @@ def test_multi_token_workspace_formula(lib, kw):
 
 def test_multi_token_split_examples(lib):
     # 2 sequences x 8 KV heads x 4 tokens x G 8 = 32 rows: 16 triples, 32768 positions
-    # -> 32 partitions of 1024, 16 * 32 * 32 rows of (128 + 2) floats
+    # -> 128 wanted, 64 of the 512-position minimum fit: 64 partitions of 512,
+    # 16 * 64 * 32 rows of (128 + 2) floats
     st, n = _mt_ws(lib, num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=2048)
-    assert st == B.PA_OK and n == 16 * 32 * 32 * 130 * 4
+    assert st == B.PA_OK and n == 16 * 64 * 32 * 130 * 4
     st, n = _mt_ws(lib, num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=2048,
                    partition_size=96)
     assert st == B.PA_OK and n == 16 * 342 * 32 * 130 * 4
