@@ -50,6 +50,9 @@ WORKLOAD_TEXT = {
     "long_bf16_bs32": "bf16 long-context split-K decode: 8 seqs, lengths uniform in "
                       "[32768, 131072], 32 q / 8 KV heads, head_dim 128, block_size 32, "
                       "512-token partitions",
+    "long_bf16_bs16_nosplit": "bf16 long-context decode without a split (one work item per "
+                              "sequence and KV head): 8 seqs, lengths uniform in [32768, "
+                              "131072], 32 q / 8 KV heads, head_dim 128, block_size 16",
     "mha_fp16": "fp16 MHA decode: 32 seqs, 32 heads, head_dim 128, block_size 16, "
                 "lengths uniform in [128, 2048]",
     "prefix_bf16": "bf16 prefix-sharing decode: 64 seqs sharing a 1024-token prefix, "
@@ -195,11 +198,45 @@ def cpu_baseline(b, kc, vc, budget_s):
         if el >= budget_s or el / runs * (runs + 1) > 3 * budget_s:
             break
     return ref, dict(value=runs * b.total_tokens() / el, unit="tokens/s", cores=threads,
-                     kind="oracle",
+                     kind="oracle", cpu_model=cpu_model(),
                      sample=f"the whole {b.name} batch (seed {b.seed}, {b.num_seqs} seqs, "
                             f"sum L = {b.total_tokens()}), after its cache write, decoded "
                             f"{runs} time(s) in {el:.1f} s by the fp64 C oracle with "
                             f"{threads} OpenMP threads")
+
+
+def copy_ceiling(nbytes=2 << 30, reps=5):
+    """A plain 2 GiB device-to-device copy (torch copy_), for context: bytes read plus
+    bytes written per second, median of ``reps`` timed copies."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    t = sorted(ts)[len(ts) // 2]
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gbps": 2 * nbytes / t / 1e9, "bytes_moved": 2 * nbytes, "seconds": t,
+            "what": "torch device-to-device copy of 2 GiB, read + write counted"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def parity(out, ref, dtype):
@@ -280,7 +317,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="minimum rotated copies of a batch")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--also", default="long_bf16_bs16,long_bf16_bs32,prefill_bf16,verify_bf16",
+    ap.add_argument("--also", default="long_bf16_bs16,long_bf16_bs32,long_bf16_bs16_nosplit,"
+                    "mha_fp16,prefix_bf16,prefill_bf16,verify_bf16",
                     help="comma-separated secondary batches measured decode-only ('' for none)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 256 MiB device-to-device copy, a dispatch of known size "
@@ -360,9 +398,15 @@ def main():
                           decode_us_p90=r["decode_ms_p90"] * 1e3,
                           algorithmic_bytes=r["decode_bytes"], achieved_gbps=r["gbps"],
                           frac_of_peak=r["gbps"] / PEAK_GBPS)
+        if rb.shared_blocks:  # prefix sharing: also the bytes as if nothing were shared
+            lb = decode_bytes(rb, unique_shared=False)
+            also[name].update(logical_bytes=lb,
+                              logical_gbps=lb / (r["decode_ms"] * 1e-3) / 1e9)
         del r
         torch.cuda.empty_cache()
 
+    copy = copy_ceiling()
+    log(f"device copy ceiling: {copy['gbps']:.0f} GB/s = {copy['gbps'] / PEAK_GBPS:.1%} of 8 TB/s")
     traffic = measured_traffic(f"{HEADLINE}/pa_decode", head["decode_bytes"])
     line = {
         "metric": METRIC,
@@ -395,6 +439,7 @@ def main():
         "parity": par,
         "step_bytes": head["decode_bytes"] + head["write_bytes"],
         "also": also,
+        "copy_ceiling": copy,
     }
     print(json.dumps(line), flush=True)
     return 0

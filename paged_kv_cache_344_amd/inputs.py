@@ -64,6 +64,12 @@ CONFIGS = {
                            head_dim=128, block_size=32, max_blocks_per_seq=4096,
                            lens=("uniform", 32768, 131072), pool=("slack", 0.10),
                            cache_write=False, partition_size=512),
+    # the same long-context batch decoded without a split: one work item per (sequence,
+    # KV head), the comparison point for the 512-token partitions
+    "long_bf16_bs16_nosplit": dict(dtype="bf16", num_seqs=8, num_q_heads=32, num_kv_heads=8,
+                                   head_dim=128, block_size=16, max_blocks_per_seq=8192,
+                                   lens=("uniform", 32768, 131072), pool=("slack", 0.10),
+                                   cache_write=False, partition_size=-1),
     # chunked prefill: a 512-token prompt chunk per sequence on top of 1024-8192 cached
     # tokens, GQA-8; every new token attends causally (pa_multi_token)
     "prefill_bf16": dict(dtype="bf16", num_seqs=8, num_q_heads=64, num_kv_heads=8,
