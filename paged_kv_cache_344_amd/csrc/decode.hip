@@ -345,6 +345,8 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       for (int nn = 0; nn < NT; ++nn) acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
       int bad = 0;
 
+      // K and V are read once per call, so their loads are non-temporal: they stay
+      // out of the way of what is reused (tables, queries, partials)
       auto issue = [&](C& c, int t0) {
         int ids[IDS];
         const int j0 = t0 / BS;
@@ -376,15 +378,15 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
         const T* pb = kbase + (int64_t)pick(rb) * blk_stride + kofs_b;
 #pragma unroll
         for (int k = 0; k < C::KL; ++k) {
-          c.ka[k] = ld16(pa + k * 4 * EPL);
-          c.kb[k] = ld16(pb + k * 4 * EPL);
+          c.ka[k] = ld16_nt(pa + k * 4 * EPL);
+          c.kb[k] = ld16_nt(pb + k * 4 * EPL);
         }
         if constexpr (BS >= 8) {
           const T* pv = vbase + (int64_t)pick(rv) * blk_stride + vofs;
 #pragma unroll
           for (int nn = 0; nn < NT; ++nn)
 #pragma unroll
-            for (int u = 0; u < C::VL; ++u) c.v[nn][u] = ld16(pv + nn * 16 * BS + u * EPL);
+            for (int u = 0; u < C::VL; ++u) c.v[nn][u] = ld16_nt(pv + nn * 16 * BS + u * EPL);
         } else {  // BS == 4: the 8 tokens straddle two blocks
           const T* lo = vbase + (int64_t)pick(2 * quad) * blk_stride + vofs;
           const T* hi = vbase + (int64_t)pick(2 * quad + 1) * blk_stride + vofs;
@@ -394,8 +396,8 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
               const u32x2 a = ld8(lo + nn * 16 * BS), b = ld8(hi + nn * 16 * BS);
               c.v[nn][0] = u32x4{a[0], a[1], b[0], b[1]};
             } else {
-              c.v[nn][0] = ld16(lo + nn * 16 * BS);
-              c.v[nn][1] = ld16(hi + nn * 16 * BS);
+              c.v[nn][0] = ld16_nt(lo + nn * 16 * BS);
+              c.v[nn][1] = ld16_nt(hi + nn * 16 * BS);
             }
           }
         }

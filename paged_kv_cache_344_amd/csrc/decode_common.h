@@ -37,6 +37,11 @@ struct Vec8<_Float16> {
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+// a 16-byte load of data read once per call (non-temporal: kept out of the way of
+// data that is reused)
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ u32x2 ld8(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }
