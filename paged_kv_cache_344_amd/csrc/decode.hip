@@ -146,6 +146,8 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   __shared__ int sm_ctotal[kSizeClasses];
   __shared__ int sm_cbase[kSizeClasses];
   __shared__ int sm_wsum[NW];
+  __shared__ int sm_wsum2[NW];
+  __shared__ int sm_pt;
   __shared__ int sm_next[2];  // by item parity: an item may pass no barrier before the next write
   __shared__ int sm_flag[2];
 
@@ -154,54 +156,74 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15;
   const int quad = lane >> 4;
-  const int S = P.num_seqs, Hq = P.num_q_heads, PT = P.part_tokens;
+  const int S = P.num_seqs, Hq = P.num_q_heads;
+  int PT = P.part_tokens;  // set by the plan when it chooses the partition size
   const int HT2 = P.num_kv_heads * P.head_tiles;
 
   // ---------------------------------------------------------------- plan
-  // thread t looks at sequences 4t .. 4t+3: number of full partitions and the class of
-  // the last one (0: an empty or invalid sequence, a one-item fill; 1: one chunk)
+  // Thread t looks at sequences 4t .. 4t+3: number of full partitions and the class of
+  // the last one (0: an empty or invalid sequence, a one-item fill; 1: one chunk;
+  // 2 .. kSizeClasses - 1 by the last partition's size).  With the default partition
+  // size both part_tokens and twice that are counted, and the longer partitions are
+  // taken when the shorter ones would give every workgroup four items or more: half
+  // the partials to write and merge, still plenty of items to balance the load.
   {
-    int nfull[4], sum = 0;
+    int nfull1[4], nfull2[4], cls1[4], cls2[4], sum1 = 0, sum2 = 0;
+    auto size_class = [&](int L, int r, int pt) {
+      return L <= 32 ? 1
+                     : 2 + (int)min((int64_t)(kSizeClasses - 3),
+                                    ((int64_t)(r - 1) * (kSizeClasses - 2)) / pt);
+    };
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = 4 * tid + i;
-      nfull[i] = 0;
+      nfull1[i] = nfull2[i] = cls1[i] = cls2[i] = 0;
       if (s < S) {
         const int L = P.seq_lens[s];
         sm_len[s] = L;
-        int cls = 0;
         if (L > 0 && L <= P.max_tokens) {
-          const int n = (L + PT - 1) / PT;
-          const int r = L - (n - 1) * PT;  // tokens in the last partition, 1..PT
-          nfull[i] = n - 1;
-          // class 1: a sequence of one chunk (its four head items can share a
-          // workgroup, one per wave); classes 2 .. 15 by the last partition's size
-          cls = L <= 32 ? 1
-                        : 2 + (int)min((int64_t)(kSizeClasses - 3),
-                                       ((int64_t)(r - 1) * (kSizeClasses - 2)) / PT);
+          const int n1 = (L + PT - 1) / PT, n2 = (L + 2 * PT - 1) / (2 * PT);
+          nfull1[i] = n1 - 1;
+          nfull2[i] = n2 - 1;
+          cls1[i] = size_class(L, L - (n1 - 1) * PT, PT);  // r: tokens in the last partition
+          cls2[i] = size_class(L, L - (n2 - 1) * 2 * PT, 2 * PT);
         }
-        sm_class[s] = cls;
       }
-      sum += nfull[i];
+      sum1 += nfull1[i];
+      sum2 += nfull2[i];
     }
-    const int incl = wave_incl_scan(sum, lane);
-    if (lane == 63) sm_wsum[wave] = incl;
+    const int incl1 = wave_incl_scan(sum1, lane);
+    const int incl2 = wave_incl_scan(sum2, lane);
+    if (lane == 63) {
+      sm_wsum[wave] = incl1;
+      sm_wsum2[wave] = incl2;
+    }
     __syncthreads();
-    int run = incl - sum;
-    for (int w = 0; w < wave; ++w) run += sm_wsum[w];
+    int F1 = 0, F2 = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      F1 += sm_wsum[w];
+      F2 += sm_wsum2[w];
+    }
+    const bool dbl = P.auto_part && (int64_t)F1 * HT2 >= 4 * (int64_t)gridDim.x;
+    int run = dbl ? incl2 - sum2 : incl1 - sum1;
+    for (int w = 0; w < wave; ++w) run += dbl ? sm_wsum2[w] : sm_wsum[w];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = 4 * tid + i;
-      if (s < S) sm_full[s] = run;
-      run += nfull[i];
+      if (s < S) {
+        sm_full[s] = run;
+        sm_class[s] = dbl ? cls2[i] : cls1[i];
+      }
+      run += dbl ? nfull2[i] : nfull1[i];
     }
     if (tid == 0) {
-      int F = 0;
-      for (int w = 0; w < NW; ++w) F += sm_wsum[w];
-      sm_full[S] = F;
+      sm_full[S] = dbl ? F2 : F1;
+      sm_pt = dbl ? 2 * PT : PT;
     }
   }
   __syncthreads();
+  PT = __builtin_amdgcn_readfirstlane(sm_pt);
   // stable counting sort of the sequences by size class, largest class first
   const int ngroups = (S + 63) / 64;
   for (int j = wave; j < ngroups; j += NW) {

@@ -275,6 +275,7 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   p.max_blocks = ext->max_blocks_per_seq;
   p.max_tokens = pl.max_tokens;
   p.part_tokens = pl.part_tokens;
+  p.auto_part = ext->partition_size == 0 ? 1 : 0;
   p.pmax = pl.pmax;
   p.nodes = pl.nodes;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);  // log2(e)

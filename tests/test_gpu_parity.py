@@ -407,3 +407,52 @@ def test_default_partitioning_workspace_reuse_is_bit_stable():
                 first[b.num_seqs] = got
             else:
                 np.testing.assert_array_equal(got, first[b.num_seqs])
+
+
+def test_many_one_chunk_partitions_parity_and_repeats():
+    """Several thousand items of one-chunk partitions (32 tokens, so three of the four
+    waves of an item have no chunk), sequences with odd and even partition counts,
+    merges over several groups of 16; three repeats on one workspace give the same bits
+    and leave the counters at zero."""
+    import paged_kv_cache_344_amd as pa
+    lens = [1, 33, 64, 65, 96, 97, 500, 1000, 2000, 3000, 3333, 4097, 5000, 6001]
+    b = inputs.make_batch("gqa_bf16", seed=24, num_seqs=len(lens), max_blocks_per_seq=376,
+                          lens=("fixed", lens), cache_write=False)
+    full = sum((L + 31) // 32 - 1 for L in lens)
+    assert full * b.num_kv_heads > 6000
+    g = OnGpu(b)
+    ws = pa.workspace_for(g.q, g.block_tables, b.num_blocks, b.block_size, b.num_kv_heads,
+                          partition_size=32)
+    ref = oracle_decode(b)
+    first = None
+    for rep in range(3):
+        say(f"one-chunk partitions rep {rep}")
+        out = torch.empty_like(g.q)
+        pa.pa_decode(g.q, g.k_cache, g.v_cache, g.block_tables, g.seq_lens, b.block_size,
+                     b.num_kv_heads, b.scale, out, workspace=ws, partition_size=32)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:_counter_bytes(b, 32)])) == 0
+        got = g.out_f64(out)
+        if first is None:
+            say(f"one-chunk partitions: {check_close(got, ref, 'bf16', 'one-chunk partitions')}")
+            first = got
+        else:
+            np.testing.assert_array_equal(got, first)
+
+
+def test_default_partitioning_doubles_with_many_items():
+    """With the default partition size and enough 512-token partitions to give each
+    workgroup four items (2224 items against 2 x 256 workgroups at bf16, head dim 128),
+    the kernel takes 1024-token partitions.  Both that and explicit 512-token partitions
+    match the oracle, and repeated default calls give the same bits."""
+    lens = [40000, 35000, 30000, 16385, 1, 513, 1025, 20000]
+    b = inputs.make_batch("gqa_bf16", seed=25, num_seqs=len(lens), num_q_heads=32,
+                          num_kv_heads=8, max_blocks_per_seq=2501, lens=("fixed", lens),
+                          cache_write=False)
+    assert sum((L + 511) // 512 - 1 for L in lens) * b.num_kv_heads == 2224
+    g = OnGpu(b)
+    ref = oracle_decode(b)
+    auto = g.out_f64(g.decode(0))
+    say(f"default partitioning, many items: {check_close(auto, ref, 'bf16', 'default, many items')}")
+    np.testing.assert_array_equal(g.out_f64(g.decode(0)), auto)
+    say(f"explicit 512: {check_close(g.out_f64(g.decode(512)), ref, 'bf16', 'explicit 512')}")
