@@ -50,6 +50,13 @@ WORKLOAD_TEXT = {
     "long_bf16_bs32": "bf16 long-context split-K decode: 8 seqs, lengths uniform in "
                       "[32768, 131072], 32 q / 8 KV heads, head_dim 128, block_size 32, "
                       "512-token partitions",
+    "long_bf16_bs16_default": "bf16 long-context split-K decode, default partitioning (1024-token "
+                              "partitions here: 512-token ones would give every workgroup four "
+                              "items or more): 8 seqs, lengths uniform in [32768, 131072], 32 q / "
+                              "8 KV heads, head_dim 128, block_size 16",
+    "long_bf16_bs32_default": "bf16 long-context split-K decode, default partitioning (1024-token "
+                              "partitions here): 8 seqs, lengths uniform in [32768, 131072], 32 q "
+                              "/ 8 KV heads, head_dim 128, block_size 32",
     "long_bf16_bs16_nosplit": "bf16 long-context decode without a split (one work item per "
                               "sequence and KV head): 8 seqs, lengths uniform in [32768, "
                               "131072], 32 q / 8 KV heads, head_dim 128, block_size 16",
@@ -142,7 +149,8 @@ class Copy:
             return
         self.decode = pa.PreparedDecode(self.q, self.kc, self.vc, self.bt, self.sl, b.block_size,
                                         b.num_kv_heads, b.scale, self.out,
-                                        partition_size=partition_size)
+                                        partition_size=partition_size,
+                                        shared_blocks=b.shared_blocks > 0)
         if b.slot_mapping is not None:
             self.kn, self.vn = t(b.k_new), t(b.v_new)
             self.sm = torch.from_numpy(b.slot_mapping).to(dev)
@@ -317,7 +325,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="minimum rotated copies of a batch")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--also", default="long_bf16_bs16,long_bf16_bs32,long_bf16_bs16_nosplit,"
+    ap.add_argument("--also", default="long_bf16_bs16,long_bf16_bs32,long_bf16_bs16_default,"
+                    "long_bf16_bs32_default,long_bf16_bs16_nosplit,"
                     "mha_fp16,prefix_bf16,prefill_bf16,verify_bf16",
                     help="comma-separated secondary batches measured decode-only ('' for none)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -393,6 +402,7 @@ def main():
             torch.cuda.empty_cache()
             continue
         also[name] = dict(workload=WORKLOAD_TEXT.get(name, name), sum_L=rb.total_tokens(),
+                          partition_size=rb.partition_size or "default",
                           tokens_per_s=rb.total_tokens() / (r["decode_ms"] * 1e-3),
                           decode_us=r["decode_ms"] * 1e3, decode_us_p10=r["decode_ms_p10"] * 1e3,
                           decode_us_p90=r["decode_ms_p90"] * 1e3,
@@ -425,7 +435,7 @@ def main():
                    "num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads,
                    "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
                    "block_size": b.block_size, "sum_L": tokens,
-                   "partition_size": b.partition_size or 512,
+                   "partition_size": b.partition_size or "default (512 tokens for this batch)",
                    "rotated_copies": head["n_copies"], "parallelism": "1 GPU"},
         "roofline": {"bound": "hbm", "achieved": head["gbps"], "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": head["gbps"] / PEAK_GBPS, "traffic": traffic,

@@ -75,13 +75,22 @@ typedef struct pa_decode_ext {
   int32_t head_dim;           /* D: 64 or 128                                          */
   int32_t max_blocks_per_seq; /* row stride of block_tables, >= 1                      */
   int64_t num_blocks;         /* N, physical blocks in the pool, >= 1                  */
-  int32_t partition_size;     /* tokens per split-K partition: 0 = 512 (default),      */
-                              /* < 0 = never split, > 0 = that many (multiple of 32)  */
+  int32_t partition_size;     /* tokens per split-K partition: 0 = default (512, or    */
+                              /* 1024 when 512-token partitions would give every     */
+                              /* workgroup four work items or more), < 0 = never     */
+                              /* split, > 0 = that many (a multiple of 32)            */
   int32_t dtype;              /* pa_dtype of q, k_cache, v_cache and out               */
   void* workspace;            /* device scratch: queue, counters, split-K partials;    */
                               /* caller-owned, zero-filled before first use            */
   size_t workspace_bytes;     /* its size; see pa_decode_workspace_bytes               */
   void* stream;               /* hipStream_t                                           */
+  int32_t shared_blocks;      /* nonzero: block tables may share physical blocks       */
+                              /* (common prefixes, parallel sampling, beam search):  */
+                              /* K/V loads keep the default cache policy so a shared */
+                              /* block read by one sequence stays cached for the     */
+                              /* others; 0: every K/V byte is read once per call and */
+                              /* is loaded non-temporally (when the launch can fill  */
+                              /* the device).  Results are the same either way.      */
 } pa_decode_ext;
 
 /*

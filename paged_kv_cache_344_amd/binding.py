@@ -30,7 +30,8 @@ class DecodeExt(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int64), ("partition_size", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p)]
+                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
+                ("shared_blocks", ctypes.c_int32)]
 
 
 class CacheWriteExt(ctypes.Structure):
@@ -177,7 +178,7 @@ class PreparedDecode:
                  block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
                  num_kv_heads: int, scale: float, out: torch.Tensor, *,
                  workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
-                 stream=None):
+                 shared_blocks: bool = False, stream=None):
         dev = q.device
         _need(dev.type == "cuda", "tensors must be on a GPU")
         for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
@@ -210,6 +211,7 @@ class PreparedDecode:
         ext.workspace = workspace.data_ptr()
         ext.workspace_bytes = workspace.numel() * workspace.element_size()
         ext.stream = _stream_ptr(dev, stream)
+        ext.shared_blocks = 1 if shared_blocks else 0
         self.ext = ext
         self.tensors = (q, k_cache, v_cache, block_tables, seq_lens, out, workspace)
         self.out = out
@@ -229,17 +231,21 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
               num_kv_heads: int, scale: float, out: torch.Tensor, *,
               workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
-              stream=None) -> torch.Tensor:
+              shared_blocks: bool = False, stream=None) -> torch.Tensor:
     """Decode attention over the paged cache (see include/pa.h for the contract).
 
     q, out [S, Hq, D]; k_cache [N, Hkv, bs, D]; v_cache [N, Hkv, D, bs];
     block_tables int32 [S, max_blocks]; seq_lens int32 [S].  All on one GPU.
     ``workspace`` is a byte tensor of at least ``pa_decode_workspace_bytes`` bytes,
     zero-filled before its first use (every call returns its counters to zero, so
-    it can be reused); when omitted, a zero-filled one is allocated for this call."""
+    it can be reused); when omitted, a zero-filled one is allocated for this call.
+    ``shared_blocks``: the tables may share physical blocks (common prefixes, parallel
+    sampling, beam search), so K/V loads keep the default cache policy; the result is
+    the same either way."""
     return PreparedDecode(q, k_cache, v_cache, block_tables, seq_lens, block_size,
                           num_kv_heads, scale, out, workspace=workspace,
-                          partition_size=partition_size, stream=stream)()
+                          partition_size=partition_size, shared_blocks=shared_blocks,
+                          stream=stream)()
 
 
 class PreparedCacheWrite:

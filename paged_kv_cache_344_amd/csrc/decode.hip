@@ -127,7 +127,10 @@ __device__ void merge_partials(const float* src_o, const float* src_ml, int64_t 
   }
 }
 
-template <typename T, int D, int BS>
+// NTL: K and V are loaded non-temporally (no table shares a block, so every byte is
+// read once per call); otherwise with the default policy, so that blocks several
+// tables share stay in L2 and the Infinity Cache for the other sequences.
+template <typename T, int D, int BS, bool NTL>
 __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_kernel(DecodeParams P) {
   typedef Chunk<T, D> C;
   constexpr int IDS = 32 / BS;  // physical blocks a 32-token chunk spans
@@ -367,8 +370,6 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       for (int nn = 0; nn < NT; ++nn) acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
       int bad = 0;
 
-      // K and V are read once per call, so their loads are non-temporal: they stay
-      // out of the way of what is reused (tables, queries, partials)
       auto issue = [&](C& c, int t0) {
         int ids[IDS];
         const int j0 = t0 / BS;
@@ -400,15 +401,15 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
         const T* pb = kbase + (int64_t)pick(rb) * blk_stride + kofs_b;
 #pragma unroll
         for (int k = 0; k < C::KL; ++k) {
-          c.ka[k] = ld16_nt(pa + k * 4 * EPL);
-          c.kb[k] = ld16_nt(pb + k * 4 * EPL);
+          c.ka[k] = ld16_as<NTL>(pa + k * 4 * EPL);
+          c.kb[k] = ld16_as<NTL>(pb + k * 4 * EPL);
         }
         if constexpr (BS >= 8) {
           const T* pv = vbase + (int64_t)pick(rv) * blk_stride + vofs;
 #pragma unroll
           for (int nn = 0; nn < NT; ++nn)
 #pragma unroll
-            for (int u = 0; u < C::VL; ++u) c.v[nn][u] = ld16_nt(pv + nn * 16 * BS + u * EPL);
+            for (int u = 0; u < C::VL; ++u) c.v[nn][u] = ld16_as<NTL>(pv + nn * 16 * BS + u * EPL);
         } else {  // BS == 4: the 8 tokens straddle two blocks
           const T* lo = vbase + (int64_t)pick(2 * quad) * blk_stride + vofs;
           const T* hi = vbase + (int64_t)pick(2 * quad + 1) * blk_stride + vofs;
@@ -418,8 +419,8 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
               const u32x2 a = ld8(lo + nn * 16 * BS), b = ld8(hi + nn * 16 * BS);
               c.v[nn][0] = u32x4{a[0], a[1], b[0], b[1]};
             } else {
-              c.v[nn][0] = ld16_nt(lo + nn * 16 * BS);
-              c.v[nn][1] = ld16_nt(hi + nn * 16 * BS);
+              c.v[nn][0] = ld16_as<NTL>(lo + nn * 16 * BS);
+              c.v[nn][1] = ld16_as<NTL>(hi + nn * 16 * BS);
             }
           }
         }
@@ -651,35 +652,36 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
 }
 
 template <typename T, int D, int BS>
-const void* kernel_of() {
-  return (const void*)decode_kernel<T, D, BS>;
+const void* kernel_of(bool stream_kv) {
+  return stream_kv ? (const void*)decode_kernel<T, D, BS, true>
+                   : (const void*)decode_kernel<T, D, BS, false>;
 }
 
 template <typename T, int D>
-const void* kernel_bs(int bs) {
+const void* kernel_bs(int bs, bool nt) {
   switch (bs) {
-    case 4: return kernel_of<T, D, 4>();
-    case 8: return kernel_of<T, D, 8>();
-    case 16: return kernel_of<T, D, 16>();
-    case 32: return kernel_of<T, D, 32>();
+    case 4: return kernel_of<T, D, 4>(nt);
+    case 8: return kernel_of<T, D, 8>(nt);
+    case 16: return kernel_of<T, D, 16>(nt);
+    case 32: return kernel_of<T, D, 32>(nt);
   }
   return nullptr;
 }
 
 template <typename T>
-const void* kernel_d(int d, int bs) {
+const void* kernel_d(int d, int bs, bool nt) {
   switch (d) {
-    case 64: return kernel_bs<T, 64>(bs);
-    case 128: return kernel_bs<T, 128>(bs);
+    case 64: return kernel_bs<T, 64>(bs, nt);
+    case 128: return kernel_bs<T, 128>(bs, nt);
   }
   return nullptr;
 }
 
-const void* decode_kernel_for(int dtype, int head_dim, int block_size) {
+const void* decode_kernel_for(int dtype, int head_dim, int block_size, bool nt) {
   switch (dtype) {
-    case 0: return kernel_d<float>(head_dim, block_size);
-    case 1: return kernel_d<_Float16>(head_dim, block_size);
-    case 2: return kernel_d<__bf16>(head_dim, block_size);
+    case 0: return kernel_d<float>(head_dim, block_size, nt);
+    case 1: return kernel_d<_Float16>(head_dim, block_size, nt);
+    case 2: return kernel_d<__bf16>(head_dim, block_size, nt);
   }
   return nullptr;
 }
@@ -688,7 +690,7 @@ const void* decode_kernel_for(int dtype, int head_dim, int block_size) {
 
 hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodeParams& p,
                          int grid, hipStream_t stream) {
-  const void* k = decode_kernel_for(dtype, head_dim, block_size);
+  const void* k = decode_kernel_for(dtype, head_dim, block_size, p.stream_kv != 0);
   if (!k || grid <= 0) return hipErrorInvalidValue;
   DecodeParams arg = p;
   void* args[] = {&arg};
@@ -696,7 +698,8 @@ hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodePa
 }
 
 hipError_t decode_blocks_per_cu(int dtype, int head_dim, int block_size, int* blocks) {
-  const void* k = decode_kernel_for(dtype, head_dim, block_size);
+  // the two cache-policy variants use the same resources
+  const void* k = decode_kernel_for(dtype, head_dim, block_size, true);
   if (!k) return hipErrorInvalidValue;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k, NT_THREADS, 0);
 }

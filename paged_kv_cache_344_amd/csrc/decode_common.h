@@ -42,6 +42,12 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
+// a 16-byte load with the non-temporal hint when NTL
+template <bool NTL>
+__device__ __forceinline__ u32x4 ld16_as(const void* p) {
+  if constexpr (NTL) return ld16_nt(p);
+  else return ld16(p);
+}
 __device__ __forceinline__ u32x2 ld8(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }

@@ -40,6 +40,7 @@ struct DecodeParams {
   int32_t max_tokens;           // max_blocks * bs
   int32_t part_tokens;          // tokens per partition, a multiple of 32
   int32_t auto_part;            // 1: default size; the kernel may double part_tokens
+  int32_t stream_kv;            // 1: no table shares a block: K/V loads are non-temporal
   int32_t pmax;                 // ceil(max_tokens / part_tokens)
   int32_t nodes;                // ceil(pmax / kMergeFan)
   float scale_log2;             // scale * log2(e): logits are kept in base-2 units
@@ -78,7 +79,6 @@ struct MultiTokenParams {
   int32_t row_tiles;            // workgroup row tiles per (sequence, KV head)
   int32_t parts;                // context partitions per (sequence, KV head); 1: no split
   int32_t part_tokens;          // tokens per partition, a multiple of 32
-  int32_t auto_part;            // 1: default size; the kernel may double part_tokens
   int32_t part_rows;            // rows stored per (row tile, partition): min(128, rows)
   float* part_o;                // [S][Hkv][row_tiles][parts][part_rows][D] unnormalised outputs
   float* part_ml;               // [S][Hkv][row_tiles][parts][part_rows][2] (max in log2 units, sum)

@@ -303,6 +303,10 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
     // no more workgroups than there can be items
     const int64_t most = (int64_t)n * pl.pmax * ht2;
     const int g = (int)std::min<int64_t>(grid, most);
+    // Non-temporal K/V loads when no table shares a block and the launch can fill the
+    // device; a launch of fewer items than resident workgroups (e.g. no split) streams
+    // each sequence through one workgroup, which the default policy serves better.
+    p.stream_kv = !ext->shared_blocks && most >= grid ? 1 : 0;
     const hipError_t e = pa::launch_decode(ext->dtype, D, block_size, p, g, stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   }

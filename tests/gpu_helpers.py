@@ -41,15 +41,19 @@ class OnGpu:
         say(f"pa_cache_write {self.b.name} seed={self.b.seed} T={self.slots.numel()}")
         pa.pa_cache_write(self.k_new, self.v_new, self.slots, self.k_cache, self.v_cache)
 
-    def decode(self, partition_size: int = 0, out=None, block_tables=None, seq_lens=None):
+    def decode(self, partition_size: int = 0, out=None, block_tables=None, seq_lens=None,
+               shared_blocks=None):
         b = self.b
         out = self.out if out is None else out
+        shared = b.shared_blocks > 0 if shared_blocks is None else shared_blocks
         say(f"pa_decode {b.name} seed={b.seed} {b.dtype} S={b.num_seqs} Hq={b.num_q_heads} "
-            f"Hkv={b.num_kv_heads} D={b.head_dim} bs={b.block_size} part={partition_size}")
+            f"Hkv={b.num_kv_heads} D={b.head_dim} bs={b.block_size} part={partition_size} "
+            f"shared_blocks={shared}")
         pa.pa_decode(self.q, self.k_cache, self.v_cache,
                      self.block_tables if block_tables is None else block_tables,
                      self.seq_lens if seq_lens is None else seq_lens, b.block_size,
-                     b.num_kv_heads, b.scale, out, partition_size=partition_size)
+                     b.num_kv_heads, b.scale, out, partition_size=partition_size,
+                     shared_blocks=shared)
         torch.cuda.synchronize()
         return out
 

@@ -150,10 +150,14 @@ def test_placement_independence_is_bit_exact():
 
 
 def test_shared_prefix_equals_private_copies_bit_exact():
+    """Tables sharing prefix blocks give the same bits as private copies of those
+    blocks, with either cache policy of the K/V loads (shared_blocks on or off)."""
     b = inputs.make_batch("prefix_bf16", seed=9, num_seqs=12, lens=("prefix", 512, 0, 300),
                           max_blocks_per_seq=51)
     g = OnGpu(b)
-    shared = g.decode().clone()
+    shared = g.decode(shared_blocks=True).clone()
+    streamed = g.decode(shared_blocks=False).clone()
+    assert torch.equal(streamed.view(torch.int16), shared.view(torch.int16))
     extra = b.shared_blocks * b.num_seqs
     kc = np.concatenate([b.k_cache, np.zeros((extra,) + b.k_cache.shape[1:], b.k_cache.dtype)])
     vc = np.concatenate([b.v_cache, np.zeros((extra,) + b.v_cache.shape[1:], b.v_cache.dtype)])
