@@ -298,8 +298,17 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   // ---------------------------------------------------------------- items
   int item = blockIdx.x;
   for (int iter = 0; item < total; ++iter) {
+    // The next item is taken from the queue when wave 0 reaches its last chunk of this
+    // one: late enough that items leave the queue in queue order (the long ones first,
+    // the short ones last) instead of being held by a workgroup for a whole item while
+    // others go idle, early enough that the atomic's round trip overlaps the last chunk
+    // and the epilogue.
     int next = 0;
-    if (tid == 0) next = (int)gridDim.x + atomicAdd(P.queue, 1);
+    bool took = false;
+    auto take_next = [&]() {
+      if (tid == 0) next = (int)gridDim.x + atomicAdd(P.queue, 1);
+      took = true;
+    };
 
     const bool tiny = item >= A && item < A + Gt;  // uniform over the workgroup
     bool active = true;                             // (tiny) this wave has an item
@@ -342,6 +351,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       // empty sequence -> zeros; a length the table cannot hold -> NaN rows
       const float fill = L == 0 ? 0.f : __builtin_nanf("");
       T* o = (T*)P.out + row0 * D;
+      take_next();
       for (int i = tid; i < nh * D; i += NT_THREADS) o[i] = (T)fill;
     } else {
       const int n = (L + PT - 1) / PT;
@@ -524,11 +534,14 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
         if (i + 1 < nc) {
           issue(B, t_of(i + 1));
           compute(A, t_of(i));
+          take_next();
           compute(B, t_of(i + 1));
         } else {
+          take_next();
           compute(A, t_of(i));
         }
       }
+      if (!took) take_next();  // (wave 0 always has a chunk; kept for safety)
 
       if (tiny) {
         // a one-chunk sequence of this wave alone: normalise and store, no merge
