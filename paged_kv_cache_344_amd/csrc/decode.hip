@@ -227,60 +227,72 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   }
   __syncthreads();
   PT = __builtin_amdgcn_readfirstlane(sm_pt);
-  // stable counting sort of the sequences by size class, largest class first
-  const int ngroups = (S + 63) / 64;
-  for (int j = wave; j < ngroups; j += NW) {
-    const int s = 64 * j + lane;
-    const int cls = s < S ? sm_class[s] : -1;
-    int c = 0;
-#pragma unroll
-    for (int b = 0; b < kSizeClasses; ++b) {
-      const int n = __popcll(__ballot(cls == b));
-      if (lane == b) c = n;
-    }
-    if (lane < kSizeClasses) sm_ccount[j][lane] = c;
-  }
-  __syncthreads();
-  if (tid < kSizeClasses) {
-    int run = 0;
-    for (int j = 0; j < ngroups; ++j) {
-      const int c = sm_ccount[j][tid];
-      sm_ccount[j][tid] = run;  // sequences of this class in earlier groups
-      run += c;
-    }
-    sm_ctotal[tid] = run;
-  }
-  __syncthreads();
-  if (tid < kSizeClasses) {
-    int base = 0;
-    for (int b = tid + 1; b < kSizeClasses; ++b) base += sm_ctotal[b];
-    sm_cbase[tid] = base;
-  }
-  __syncthreads();
-  for (int j = wave; j < ngroups; j += NW) {
-    const int s = 64 * j + lane;
-    const int cls = s < S ? sm_class[s] : -1;
-    uint64_t same = 0;
-#pragma unroll
-    for (int b = 0; b < kSizeClasses; ++b) {
-      const uint64_t m = __ballot(cls == b);
-      if (cls == b) same = m;
-    }
-    if (s < S) {
-      const int rank = __popcll(same & ((1ull << lane) - 1ull));
-      sm_last[sm_cbase[cls] + sm_ccount[j][cls] + rank] = s;
-    }
-  }
-  __syncthreads();
+  // Stable counting sort of the sequences by size class, largest class first, and the
+  // queue layout it gives: regular items (full partitions, then last partitions by
+  // decreasing size), then one-chunk sequences NW items to a workgroup (one per wave),
+  // then the fill items of empty or invalid sequences.
   const int F = sm_full[S];
-  // Queue order: regular items (full partitions, then last partitions by decreasing
-  // size), then one-chunk sequences NW items to a workgroup (one per wave), then the
-  // fill items of empty or invalid sequences.
-  const int c0 = sm_ctotal[0], c1 = sm_ctotal[1];
-  const int jt0 = F + S - c0 - c1;            // first one-chunk entry
-  const int A = jt0 * HT2;                    // regular items
-  const int Gt = (c1 * HT2 + NW - 1) / NW;    // groups of one-chunk items
-  const int total = A + Gt + c0 * HT2;        // the host keeps (F + S) * HT2 below 2^31
+  int c0 = 0, c1 = 0, jt0 = 0, A = 0, Gt = 0, total = 0;
+  auto finish_plan = [&]() {
+    const int ngroups = (S + 63) / 64;
+    for (int j = wave; j < ngroups; j += NW) {
+      const int s = 64 * j + lane;
+      const int cls = s < S ? sm_class[s] : -1;
+      int c = 0;
+#pragma unroll
+      for (int b = 0; b < kSizeClasses; ++b) {
+        const int n = __popcll(__ballot(cls == b));
+        if (lane == b) c = n;
+      }
+      if (lane < kSizeClasses) sm_ccount[j][lane] = c;
+    }
+    __syncthreads();
+    if (tid < kSizeClasses) {
+      int run = 0;
+      for (int j = 0; j < ngroups; ++j) {
+        const int c = sm_ccount[j][tid];
+        sm_ccount[j][tid] = run;  // sequences of this class in earlier groups
+        run += c;
+      }
+      sm_ctotal[tid] = run;
+    }
+    __syncthreads();
+    if (tid < kSizeClasses) {
+      int base = 0;
+      for (int b = tid + 1; b < kSizeClasses; ++b) base += sm_ctotal[b];
+      sm_cbase[tid] = base;
+    }
+    __syncthreads();
+    for (int j = wave; j < ngroups; j += NW) {
+      const int s = 64 * j + lane;
+      const int cls = s < S ? sm_class[s] : -1;
+      uint64_t same = 0;
+#pragma unroll
+      for (int b = 0; b < kSizeClasses; ++b) {
+        const uint64_t m = __ballot(cls == b);
+        if (cls == b) same = m;
+      }
+      if (s < S) {
+        const int rank = __popcll(same & ((1ull << lane) - 1ull));
+        sm_last[sm_cbase[cls] + sm_ccount[j][cls] + rank] = s;
+      }
+    }
+    __syncthreads();
+    c0 = sm_ctotal[0];
+    c1 = sm_ctotal[1];
+    jt0 = F + S - c0 - c1;            // first one-chunk entry
+    A = jt0 * HT2;                    // regular items
+    Gt = (c1 * HT2 + NW - 1) / NW;    // groups of one-chunk items
+    total = A + Gt + c0 * HT2;        // the host keeps (F + S) * HT2 below 2^31
+  };
+  // A workgroup whose first item is a full partition (known from the scan alone) sorts
+  // after issuing that item's first loads, so that the sort runs while they are in
+  // flight; the others sort first.
+  bool planned = false;
+  if ((int64_t)blockIdx.x >= (int64_t)F * HT2) {
+    finish_plan();
+    planned = true;
+  }
 
   // table entries are int32, so a pool larger than INT32_MAX blocks accepts them all
   const uint32_t nblk32 = (uint32_t)min(P.num_blocks, (int64_t)0x7fffffff);
@@ -297,7 +309,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
 
   // ---------------------------------------------------------------- items
   int item = blockIdx.x;
-  for (int iter = 0; item < total; ++iter) {
+  for (int iter = 0; !planned || item < total; ++iter) {
     // The next item is taken from the queue when wave 0 reaches its last chunk of this
     // one: late enough that items leave the queue in queue order (the long ones first,
     // the short ones last) instead of being held by a workgroup for a whole item while
@@ -310,7 +322,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       took = true;
     };
 
-    const bool tiny = item >= A && item < A + Gt;  // uniform over the workgroup
+    const bool tiny = planned && item >= A && item < A + Gt;  // uniform over the workgroup
     bool active = true;                             // (tiny) this wave has an item
     int j, gt;
     if (tiny) {
@@ -320,7 +332,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       j = jt0 + uu / HT2;
       gt = uu - (uu / HT2) * HT2;
     } else {
-      const int idx = item < A ? item : item - Gt + c1 * HT2;
+      const int idx = !planned || item < A ? item : item - Gt + c1 * HT2;
       j = idx / HT2;
       gt = idx - j * HT2;
     }
@@ -522,25 +534,31 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       const int nc = tiny ? (active ? 1 : 0) : wave < nchunks ? (nchunks - wave + NW - 1) / NW : 0;
       auto t_of = [&](int i) { return tiny ? 0 : t_begin + 32 * (wave + NW * i); };
       if (nc > 0) {
-        C A, B;
-        issue(A, t_of(0));
+        C CA, CB;  // the two chunk buffers
+        issue(CA, t_of(0));
+        // this workgroup's first item: sort while CA loads (the other branch takes
+        // the same barriers)
+        if (!planned) finish_plan();
         int i = 0;
         for (; i + 2 < nc; i += 2) {
-          issue(B, t_of(i + 1));
-          compute(A, t_of(i));
-          issue(A, t_of(i + 2));
-          compute(B, t_of(i + 1));
+          issue(CB, t_of(i + 1));
+          compute(CA, t_of(i));
+          issue(CA, t_of(i + 2));
+          compute(CB, t_of(i + 1));
         }
         if (i + 1 < nc) {
-          issue(B, t_of(i + 1));
-          compute(A, t_of(i));
+          issue(CB, t_of(i + 1));
+          compute(CA, t_of(i));
           take_next();
-          compute(B, t_of(i + 1));
+          compute(CB, t_of(i + 1));
         } else {
           take_next();
-          compute(A, t_of(i));
+          compute(CA, t_of(i));
         }
+      } else if (!planned) {
+        finish_plan();
       }
+      planned = true;
       if (!took) take_next();  // (wave 0 always has a chunk; kept for safety)
 
       if (tiny) {
@@ -649,6 +667,10 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
 
     // Two slots: thread 0 may write the next item's slot before a slow wave has read
     // this one only if the item in between passes no barrier (the fill path).
+    if (!planned) {  // (not reached: the first item of such a workgroup is a full one)
+      finish_plan();
+      planned = true;
+    }
     if (tid == 0) sm_next[iter & 1] = next;
     __syncthreads();  // also: every thread is done with this item's LDS
     item = sm_next[iter & 1];
