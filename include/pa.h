@@ -335,7 +335,7 @@ const char* pa_last_error(void);
 /* ABI version of this header: bumped on any incompatible change. */
 int32_t pa_abi_version(void);
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2  /* 2: pa_decode_ext.shared_blocks */
 
 #ifdef __cplusplus
 }

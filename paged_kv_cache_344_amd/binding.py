@@ -16,6 +16,7 @@ from .build import LIB_PATH, INCLUDE
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_CAPACITY = range(6)
 PA_F32, PA_F16, PA_BF16 = range(3)
+ABI_VERSION = 2  # PA_ABI_VERSION of the header these structures mirror
 TORCH_DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
 
@@ -106,6 +107,9 @@ def lib():
         L.pa_last_error.restype = ctypes.c_char_p
         L.pa_abi_version.argtypes = []
         L.pa_abi_version.restype = ctypes.c_int32
+        if L.pa_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.pa_abi_version()}, this binding "
+                               f"expects {ABI_VERSION}: rebuild the library")
         _lib = L
     return _lib
 

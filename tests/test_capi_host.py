@@ -2,6 +2,8 @@
 function include/pa.h declares, and rejects bad arguments with the documented status
 before any HIP call (so fake, never-dereferenced pointers are safe here)."""
 import ctypes
+import os
+import subprocess
 
 import pytest
 
@@ -21,7 +23,36 @@ def test_exports_every_declared_function(lib):
             "pa_last_error", "pa_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == B.ABI_VERSION
+    head = open(os.path.join(B.INCLUDE, "pa.h")).read()
+    assert f"#define PA_ABI_VERSION {B.ABI_VERSION}" in head
+
+
+def test_ext_struct_layouts_match_the_header(tmp_path):
+    """Every field of the ctypes mirrors of the ext structs sits at the offset the C
+    compiler gives it in include/pa.h, and the sizes agree (a plain C program built with
+    gcc against the header prints them)."""
+    structs = {"pa_decode_ext": B.DecodeExt, "pa_cache_write_ext": B.CacheWriteExt,
+               "pa_multi_token_ext": B.MultiTokenExt, "pa_copy_blocks_ext": B.CopyBlocksExt}
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "pa.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", B.INCLUDE, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    got = {}
+    for line in out.splitlines():
+        cname, field, val = line.split()
+        got[(cname, field)] = int(val)
+    for cname, py in structs.items():
+        assert got[(cname, "sizeof")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
 
 
 def test_status_strings(lib):
