@@ -14,7 +14,10 @@ Reported (one JSON line on stdout):
   roofline   the decode call timed with HIP events on the stream it runs on, inside
              the same timed region: algorithmic bytes per call / mean call duration,
              against 8 TB/s
-  cpu_baseline  the fp64 oracle on the host cores, on the same batch
+  cpu_baseline  the fp64 oracle on the host cores, on the same batch (and one decode of
+             it on one thread, for context)
+  cache_write   the headline step's pa_cache_write alone (128 tokens), event-timed
+  tiny_fp32     the tiny fp32 batch: cache write, decode, and the two as a pair
   parity     GPU output of the last timed step against the oracle
   also       the same decode-only measurement for the long-context batches, and the
              chunked-prefill and draft-verification batches through pa_multi_token
@@ -205,12 +208,63 @@ def cpu_baseline(b, kc, vc, budget_s):
         el = time.perf_counter() - t0
         if el >= budget_s or el / runs * (runs + 1) > 3 * budget_s:
             break
+    # one thread, for context: one decode of the same batch
+    oracle.set_threads(1)
+    t1 = time.perf_counter()
+    oracle.decode(b.q, kc, vc, b.block_tables, b.seq_lens, b.block_size, b.num_kv_heads,
+                  b.scale, b.dtype)
+    el1 = time.perf_counter() - t1
+    oracle.set_threads(threads)
     return ref, dict(value=runs * b.total_tokens() / el, unit="tokens/s", cores=threads,
                      kind="oracle", cpu_model=cpu_model(),
                      sample=f"the whole {b.name} batch (seed {b.seed}, {b.num_seqs} seqs, "
                             f"sum L = {b.total_tokens()}), after its cache write, decoded "
                             f"{runs} time(s) in {el:.1f} s by the fp64 C oracle with "
-                            f"{threads} OpenMP threads")
+                            f"{threads} OpenMP threads",
+                     single_thread={"value": b.total_tokens() / el1, "unit": "tokens/s",
+                                    "sample": f"one decode of the same batch on 1 thread "
+                                              f"({el1:.2f} s)"})
+
+
+def time_calls(calls, n):
+    """Event-timed calls (each a zero-argument callable), run in turn n times; returns
+    the sorted durations in microseconds."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for k in range(n):
+        ev[k][0].record()
+        calls[k % len(calls)]()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(z) * 1e3 for a, z in ev)
+
+
+def summary_us(ts):
+    return {"mean_us": sum(ts) / len(ts), "p10_us": ts[len(ts) // 10],
+            "p90_us": ts[(9 * len(ts)) // 10]}
+
+
+def tiny_pair(seed, n):
+    """The tiny fp32 correctness batch (4 sequences, one new token each): cache write
+    alone, decode alone, and the write + decode pair, event-timed (launch-bound)."""
+    import torch
+    from paged_kv_cache_344_amd import inputs
+    b = inputs.make_batch("tiny_fp32", seed=seed)
+    c = Copy(b, 0)
+    for _ in range(5):
+        c.write()
+        c.decode()
+    torch.cuda.synchronize()
+
+    def pair():
+        c.write()
+        c.decode()
+    return dict(workload="fp32 tiny batch: 4 seqs, lengths {5, 10, 17, 33}, block_size 4, "
+                         "2 heads (MHA), head_dim 64; one new token per sequence",
+                cache_write=summary_us(time_calls([c.write], n)),
+                decode=summary_us(time_calls([c.decode], n)),
+                write_then_decode=summary_us(time_calls([pair], n)))
 
 
 def copy_ceiling(nbytes=2 << 30, reps=5):
@@ -360,6 +414,13 @@ def main():
     tokens = b.total_tokens()
     value = args.steps * tokens / head["elapsed"]
 
+    # the cache write of the headline step alone (same copies, same slots each time)
+    cw = summary_us(time_calls([c.write for c in head["copies"]], max(50, args.steps // 2)))
+    cw_bytes = cache_write_bytes(b)
+    cw.update(tokens=int(b.slot_mapping.shape[0]), bytes=cw_bytes,
+              gbps=cw_bytes / (cw["mean_us"] * 1e-6) / 1e9)
+    log(f"cache write alone: {cw['mean_us']:.1f} us for {cw['tokens']} tokens")
+
     kc, vc = oracle_reference(b)
     if args.no_cpu_baseline:
         import oracle
@@ -415,6 +476,8 @@ def main():
         del r
         torch.cuda.empty_cache()
 
+    tiny = tiny_pair(args.seed, 100)
+    log(f"tiny batch: write + decode {tiny['write_then_decode']['mean_us']:.1f} us")
     copy = copy_ceiling()
     log(f"device copy ceiling: {copy['gbps']:.0f} GB/s = {copy['gbps'] / PEAK_GBPS:.1%} of 8 TB/s")
     traffic = measured_traffic(f"{HEADLINE}/pa_decode", head["decode_bytes"])
@@ -448,6 +511,8 @@ def main():
         "cpu_baseline": cpu,
         "parity": par,
         "step_bytes": head["decode_bytes"] + head["write_bytes"],
+        "cache_write": cw,
+        "tiny_fp32": tiny,
         "also": also,
         "copy_ceiling": copy,
     }
