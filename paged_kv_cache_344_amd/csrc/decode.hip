@@ -308,6 +308,51 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   const int vofs = (BS >= 8) ? col * BS + (8 * quad) % BS : col * BS;
 
   // ---------------------------------------------------------------- items
+  // A split item's arrival in its merge group is issued at the end of the item, but its
+  // answer (was this the group's last member?) is read only when the workgroup next
+  // settles: at the start of its next item, once that item's first loads have gone out,
+  // or after the item loop.  The atomic's round trip then runs under those loads instead
+  // of stalling the workgroup.  The member that completed a group merges it there.
+  bool pend = false;   // (uniform) an arrival whose answer has not been read
+  int pend_before = 0;  // (thread 0) the arrival's answer: members counted before it
+  int pend_s = 0, pend_gt = 0, pend_grp = 0, pend_gsize = 0, pend_ngrp = 0, pend_nh = 0,
+      pend_n = 0;
+  int64_t pend_row0 = 0;
+  auto settle = [&]() {
+    if (tid == 0) {
+      const int done = pend_before == pend_gsize - 1;
+      // every member has arrived: ready for the next call
+      if (done) atomicExch(P.node_count + ((int64_t)pend_s * HT2 + pend_gt) * P.nodes + pend_grp, 0);
+      sm_flag[0] = done;
+    }
+    __syncthreads();
+    if (sm_flag[0]) {
+      if (pend_ngrp == 1) {
+        merge_partials<T, D>(P.part_o, P.part_ml, pend_row0, P.pmax, 0, pend_n, pend_nh,
+                             (T*)P.out, nullptr, nullptr, 0, 0, Hq);
+      } else {
+        merge_partials<T, D>(P.part_o, P.part_ml, pend_row0, P.pmax, pend_grp * kMergeFan,
+                             pend_gsize, pend_nh, (T*)nullptr, P.node_o, P.node_ml, P.nodes,
+                             pend_grp, Hq);
+        stores_done();
+        __syncthreads();
+        if (tid == 0) {
+          int* cnt = P.root_count + (int64_t)pend_s * HT2 + pend_gt;
+          const int before = atomicAdd(cnt, 1);
+          const int done = before == pend_ngrp - 1;
+          if (done) atomicExch(cnt, 0);
+          sm_flag[1] = done;
+        }
+        __syncthreads();
+        if (sm_flag[1]) {
+          merge_partials<T, D>(P.node_o, P.node_ml, pend_row0, P.nodes, 0, pend_ngrp, pend_nh,
+                               (T*)P.out, nullptr, nullptr, 0, 0, Hq);
+        }
+      }
+    }
+    pend = false;
+  };
+
   int item = blockIdx.x;
   for (int iter = 0; !planned || item < total; ++iter) {
     // The next item is taken from the queue when wave 0 reaches its last chunk of this
@@ -536,9 +581,10 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       if (nc > 0) {
         C CA, CB;  // the two chunk buffers
         issue(CA, t_of(0));
-        // this workgroup's first item: sort while CA loads (the other branch takes
-        // the same barriers)
+        // this workgroup's first item: sort while CA loads; a pending arrival is
+        // settled here too (the other branch takes the same barriers)
         if (!planned) finish_plan();
+        if (pend) settle();
         int i = 0;
         for (; i + 2 < nc; i += 2) {
           issue(CB, t_of(i + 1));
@@ -555,8 +601,9 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
           take_next();
           compute(CA, t_of(i));
         }
-      } else if (!planned) {
-        finish_plan();
+      } else {
+        if (!planned) finish_plan();
+        if (pend) settle();
       }
       planned = true;
       if (!took) take_next();  // (wave 0 always has a chunk; kept for safety)
@@ -624,43 +671,22 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       }
 
       if (n > 1) {
-        // publish this partition, then count it in its group of kMergeFan
+        // publish this partition, then count it in its group of kMergeFan; the answer
+        // is read when this workgroup next settles
         stores_done();
         __syncthreads();
         const int grp = p / kMergeFan;
-        const int gsize = min(kMergeFan, n - grp * kMergeFan);
-        const int ngrp = (n + kMergeFan - 1) / kMergeFan;
-        if (tid == 0) {
-          int* cnt = P.node_count + ((int64_t)s * HT2 + gt) * P.nodes + grp;
-          const int before = atomicAdd(cnt, 1);
-          const int done = before == gsize - 1;
-          if (done) atomicExch(cnt, 0);  // every member has arrived: ready for the next call
-          sm_flag[0] = done;
-        }
-        __syncthreads();
-        if (sm_flag[0]) {
-          if (ngrp == 1) {
-            merge_partials<T, D>(P.part_o, P.part_ml, row0, P.pmax, 0, n, nh, (T*)P.out,
-                                 nullptr, nullptr, 0, 0, Hq);
-          } else {
-            merge_partials<T, D>(P.part_o, P.part_ml, row0, P.pmax, grp * kMergeFan, gsize, nh,
-                                 (T*)nullptr, P.node_o, P.node_ml, P.nodes, grp, Hq);
-            stores_done();
-            __syncthreads();
-            if (tid == 0) {
-              int* cnt = P.root_count + (int64_t)s * HT2 + gt;
-              const int before = atomicAdd(cnt, 1);
-              const int done = before == ngrp - 1;
-              if (done) atomicExch(cnt, 0);
-              sm_flag[1] = done;
-            }
-            __syncthreads();
-            if (sm_flag[1]) {
-              merge_partials<T, D>(P.node_o, P.node_ml, row0, P.nodes, 0, ngrp, nh, (T*)P.out,
-                                   nullptr, nullptr, 0, 0, Hq);
-            }
-          }
-        }
+        if (tid == 0)
+          pend_before = atomicAdd(P.node_count + ((int64_t)s * HT2 + gt) * P.nodes + grp, 1);
+        pend = true;
+        pend_s = s;
+        pend_gt = gt;
+        pend_grp = grp;
+        pend_gsize = min(kMergeFan, n - grp * kMergeFan);
+        pend_ngrp = (n + kMergeFan - 1) / kMergeFan;
+        pend_nh = nh;
+        pend_n = n;
+        pend_row0 = row0;
       }
       }  // not a one-chunk group
     }
@@ -675,6 +701,8 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
     __syncthreads();  // also: every thread is done with this item's LDS
     item = sm_next[iter & 1];
   }
+
+  if (pend) settle();
 
   // the last workgroup out resets the queue for the next call
   if (tid == 0) {
