@@ -211,11 +211,19 @@ typedef __attribute__((address_space(3))) void lds_void;
 // inline assembly so that the compiler's wait insertion, which cannot tell the chunk
 // buffers apart, does not wait for every load in flight before each LDS read; the waits
 // for these loads are the pipeline's own (wait_loads_and_sync).
-template <int SIZE>
+// With NTL the load is non-temporal: for K/V that no other workgroup reads.
+template <int SIZE, bool NTL>
 __device__ __forceinline__ void load_to_lds(const void* g, const void* lds) {
   const uint32_t m = (uint32_t)(uintptr_t)(lds_void*)lds;
-  if constexpr (SIZE == 16) {
+  if constexpr (SIZE == 16 && NTL) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 ::"s"(m), "v"(g) : "memory", "m0");
+  } else if constexpr (SIZE == 16) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 ::"s"(m), "v"(g) : "memory", "m0");
+  } else if constexpr (NTL) {
+    static_assert(SIZE == 4, "16- or 4-byte loads");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off nt"
                  ::"s"(m), "v"(g) : "memory", "m0");
   } else {
     static_assert(SIZE == 4, "16- or 4-byte loads");
@@ -235,7 +243,10 @@ __device__ __forceinline__ void wait_loads_and_sync() {
 }
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <typename T, int D, int BS>
+// NTL: K/V staging loads are non-temporal.  Used when each (sequence, KV head) has one
+// row tile, so every K/V byte is read by one workgroup (draft-token verification);
+// several row tiles share each chunk through L2 (prompt chunks) and keep the default.
+template <typename T, int D, int BS, bool NTL>
 __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_kernel(MultiTokenParams P) {
   typedef Shape<T, D, BS> SH;
   constexpr int KL = SH::KL, NT = SH::NT, EPL = SH::EPL, KSEG = SH::KSEG, TPS = SH::TPS;
@@ -389,7 +400,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
         const int id1 = checked(kid[i][1]);
         id = lane >= 32 ? id1 : id;
       }
-      load_to_lds<16>(kbase + (int64_t)id * blk_stride + koff[i],
+      load_to_lds<16, NTL>(kbase + (int64_t)id * blk_stride + koff[i],
                       &sk[buf][64 * (wave + WAVES * i) * EPL]);
     }
 #pragma unroll
@@ -399,7 +410,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
         const int id1 = checked(vid[i][1]);
         id = (lane & 2) ? id1 : id;
       }
-      load_to_lds<SH::VB>(vbase + (int64_t)id * blk_stride + voff[i],
+      load_to_lds<SH::VB, NTL>(vbase + (int64_t)id * blk_stride + voff[i],
                           &sv[buf][64 * (wave + WAVES * i) * SH::VB / SH::E]);
     }
   };
@@ -668,31 +679,37 @@ __global__ __launch_bounds__(THREADS) void multi_token_merge_kernel(MultiTokenPa
   store4(o, nan_seen ? f32x4{nan, nan, nan, nan} : O / Ls);
 }
 
+template <typename T, int D, int BS>
+const void* mt_nt(bool nt) {
+  return nt ? (const void*)multi_token_kernel<T, D, BS, true>
+            : (const void*)multi_token_kernel<T, D, BS, false>;
+}
+
 template <typename T, int D>
-const void* mt_bs(int bs) {
+const void* mt_bs(int bs, bool nt) {
   switch (bs) {
-    case 4: return (const void*)multi_token_kernel<T, D, 4>;
-    case 8: return (const void*)multi_token_kernel<T, D, 8>;
-    case 16: return (const void*)multi_token_kernel<T, D, 16>;
-    case 32: return (const void*)multi_token_kernel<T, D, 32>;
+    case 4: return mt_nt<T, D, 4>(nt);
+    case 8: return mt_nt<T, D, 8>(nt);
+    case 16: return mt_nt<T, D, 16>(nt);
+    case 32: return mt_nt<T, D, 32>(nt);
   }
   return nullptr;
 }
 
 template <typename T>
-const void* mt_d(int d, int bs) {
+const void* mt_d(int d, int bs, bool nt) {
   switch (d) {
-    case 64: return mt_bs<T, 64>(bs);
-    case 128: return mt_bs<T, 128>(bs);
+    case 64: return mt_bs<T, 64>(bs, nt);
+    case 128: return mt_bs<T, 128>(bs, nt);
   }
   return nullptr;
 }
 
-const void* multi_token_kernel_for(int dtype, int head_dim, int block_size) {
+const void* multi_token_kernel_for(int dtype, int head_dim, int block_size, bool nt) {
   switch (dtype) {
-    case 0: return mt_d<float>(head_dim, block_size);
-    case 1: return mt_d<_Float16>(head_dim, block_size);
-    case 2: return mt_d<__bf16>(head_dim, block_size);
+    case 0: return mt_d<float>(head_dim, block_size, nt);
+    case 1: return mt_d<_Float16>(head_dim, block_size, nt);
+    case 2: return mt_d<__bf16>(head_dim, block_size, nt);
   }
   return nullptr;
 }
@@ -733,7 +750,7 @@ hipError_t launch_multi_token_merge(int dtype, int head_dim, const MultiTokenPar
 
 hipError_t launch_multi_token(int dtype, int head_dim, int block_size, MultiTokenParams p,
                               hipStream_t stream) {
-  const void* k = multi_token_kernel_for(dtype, head_dim, block_size);
+  const void* k = multi_token_kernel_for(dtype, head_dim, block_size, p.row_tiles == 1);
   const int64_t groups = (int64_t)p.num_kv_heads * p.num_seqs;
   const int64_t per_xcd = (groups + XCDS - 1) / XCDS * p.row_tiles * p.parts;
   if (!k || groups <= 0 || p.row_tiles <= 0 || p.parts <= 0 || per_xcd * XCDS > 0x7fffffff)
