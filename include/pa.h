@@ -118,7 +118,8 @@ typedef struct pa_decode_ext {
  *   out           [S][Hq][D]                 dtype; written, rounded to nearest even
  *
  * Arithmetic: fp32 accumulation everywhere.  For f16 / bf16 the softmax weights
- * are rounded to the input dtype before the weighted sum (matrix-core input).
+ * enter the weighted sum (a matrix-core product) as a hi + lo pair of the input
+ * dtype, about 16 significant bits; the only rounding left is the output's.
  * Long sequences are split into partitions of partition_size tokens; each
  * partition keeps (running max, running sum, unnormalised output) in the
  * workspace, and the partitions are combined with log-sum-exp weights along a
@@ -149,6 +150,8 @@ typedef struct pa_decode_ext {
  * Execution: one persistent launch per 1024 sequences (about as many workgroups
  * as are resident on the device at once), each planning from seq_lens which
  * partitions hold tokens and taking work items from a queue in the workspace.
+ * K/V loads are non-temporal unless ext->shared_blocks is set or the launch has
+ * fewer possible items than resident workgroups; results are the same either way.
  */
 pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* seq_lens, int32_t block_size,

@@ -12,8 +12,10 @@
 // ([ASP] 实现要点, the kernel that takes a block table).  Inside a block the reads
 // are contiguous ([ASP] 核心思想).
 //
-// Work items.  A sequence is cut into partitions of part_tokens tokens; a work item
-// is (sequence, partition, KV head, tile of up to 16 of its query heads) and is
+// Work items.  A sequence is cut into partitions of part_tokens tokens (with the
+// default size, twice that when the shorter partitions would give every workgroup
+// four items or more: half the partials to write and merge); a work item is
+// (sequence, partition, KV head, tile of up to 16 of its query heads) and is
 // handled by one 4-wave workgroup.  The launch is persistent: about as many
 // workgroups as fit on the chip at once, each taking items from a queue counter
 // until none are left.  Lengths live in device memory, so every workgroup first
@@ -23,7 +25,9 @@
 // decreasing size, so that the last items to start are the short ones.  Sequences of a
 // single 32-token chunk come after those, four (sequence, head tile) items to a
 // workgroup, one per wave, each wave finishing its own item without the LDS merge.
-// Every workgroup computes the same plan.
+// Every workgroup computes the same plan.  A workgroup takes its next item when wave 0
+// reaches its last chunk of the current one, so that items leave the queue in queue
+// order rather than being held while other workgroups run dry.
 //
 // Inside an item the four waves take 32-token chunks in turn.  The G query heads of
 // one KV head share every K/V byte, so the logits of a chunk are a (tokens x D) by
@@ -54,11 +58,16 @@
 // softmax weights enter the weighted sum as a bf16/f16 hi + lo pair (two MFMAs),
 // which keeps them to about fp32 accuracy.
 //
+// Cache policy.  With no block shared between tables, every K/V byte is read once per
+// call and the loads are non-temporal (NTL); shared blocks keep the default policy so
+// that they stay cached for the other sequences.
+//
 // Split-K merge.  A sequence with one partition is finished by its only item.
 // Otherwise each item stores (max, sum, unnormalised output) per head; partitions
 // form groups of 16, and the item that completes a group (an arrival counter)
 // combines the group with log-sum-exp weights, and the item that completes the
-// last group combines the groups.  The tree is fixed by partition numbers, so the
+// last group combines the groups.  The group arrival's answer is read at the
+// workgroup's next item start, under that item's first loads.  The tree is fixed by partition numbers, so the
 // result does not depend on timing or on which workgroup ran what.  Counters are
 // reset by whoever finishes them, so they are all zero again after a call.
 #include <math.h>
