@@ -53,11 +53,11 @@ WORKLOAD_TEXT = {
     "long_bf16_bs32": "bf16 long-context split-K decode: 8 seqs, lengths uniform in "
                       "[32768, 131072], 32 q / 8 KV heads, head_dim 128, block_size 32, "
                       "512-token partitions",
-    "long_bf16_bs16_default": "bf16 long-context split-K decode, default partitioning (1024-token "
-                              "partitions here: 512-token ones would give every workgroup four "
-                              "items or more): 8 seqs, lengths uniform in [32768, 131072], 32 q / "
-                              "8 KV heads, head_dim 128, block_size 16",
-    "long_bf16_bs32_default": "bf16 long-context split-K decode, default partitioning (1024-token "
+    "long_bf16_bs16_default": "bf16 long-context split-K decode, default partitioning (sized "
+                              "on the device from the lengths: 6144-token partitions here): 8 "
+                              "seqs, lengths uniform in [32768, 131072], 32 q / 8 KV heads, "
+                              "head_dim 128, block_size 16",
+    "long_bf16_bs32_default": "bf16 long-context split-K decode, default partitioning (6144-token "
                               "partitions here): 8 seqs, lengths uniform in [32768, 131072], 32 q "
                               "/ 8 KV heads, head_dim 128, block_size 32",
     "long_bf16_bs16_nosplit": "bf16 long-context decode without a split (one work item per "
@@ -498,7 +498,7 @@ def main():
                    "num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads,
                    "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
                    "block_size": b.block_size, "sum_L": tokens,
-                   "partition_size": b.partition_size or "default (512 tokens for this batch)",
+                   "partition_size": b.partition_size or "default (768 tokens for this batch)",
                    "rotated_copies": head["n_copies"], "parallelism": "1 GPU"},
         "roofline": {"bound": "hbm", "achieved": head["gbps"], "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": head["gbps"] / PEAK_GBPS, "traffic": traffic,

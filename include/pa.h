@@ -75,10 +75,11 @@ typedef struct pa_decode_ext {
   int32_t head_dim;           /* D: 64 or 128                                          */
   int32_t max_blocks_per_seq; /* row stride of block_tables, >= 1                      */
   int64_t num_blocks;         /* N, physical blocks in the pool, >= 1                  */
-  int32_t partition_size;     /* tokens per split-K partition: 0 = default (512, or    */
-                              /* 1024 when 512-token partitions would give every     */
-                              /* workgroup four work items or more), < 0 = never     */
-                              /* split, > 0 = that many (a multiple of 32)            */
+  int32_t partition_size;     /* tokens per split-K partition: 0 = default (chosen on  */
+                              /* the device from the lengths: 3/4 of one workgroup's */
+                              /* even share of the work, in steps of 256, at least   */
+                              /* 512), < 0 = never split, > 0 = that many (a multiple */
+                              /* of 32)                                               */
   int32_t dtype;              /* pa_dtype of q, k_cache, v_cache and out               */
   void* workspace;            /* device scratch: queue, counters, split-K partials;    */
                               /* caller-owned, zero-filled before first use            */

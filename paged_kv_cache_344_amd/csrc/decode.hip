@@ -13,8 +13,7 @@
 // are contiguous ([ASP] 核心思想).
 //
 // Work items.  A sequence is cut into partitions of part_tokens tokens (with the
-// default size, twice that when the shorter partitions would give every workgroup
-// four items or more: half the partials to write and merge); a work item is
+// default size, as long as the load balance allows: see the plan); a work item is
 // (sequence, partition, KV head, tile of up to 16 of its query heads) and is
 // handled by one 4-wave workgroup.  The launch is persistent: about as many
 // workgroups as fit on the chip at once, each taking items from a queue counter
@@ -158,8 +157,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   __shared__ int sm_ctotal[kSizeClasses];
   __shared__ int sm_cbase[kSizeClasses];
   __shared__ int sm_wsum[NW];
-  __shared__ int sm_wsum2[NW];
-  __shared__ int sm_pt;
+  __shared__ float sm_wsumf[NW];
   __shared__ int sm_next[2];  // by item parity: an item may pass no barrier before the next write
   __shared__ int sm_flag[2];
 
@@ -173,69 +171,79 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   const int HT2 = P.num_kv_heads * P.head_tiles;
 
   // ---------------------------------------------------------------- plan
-  // Thread t looks at sequences 4t .. 4t+3: number of full partitions and the class of
-  // the last one (0: an empty or invalid sequence, a one-item fill; 1: one chunk;
-  // 2 .. kSizeClasses - 1 by the last partition's size).  With the default partition
-  // size both part_tokens and twice that are counted, and the longer partitions are
-  // taken when the shorter ones would give every workgroup four items or more: half
-  // the partials to write and merge, still plenty of items to balance the load.
+  // Thread t looks at sequences 4t .. 4t+3.  With the default partition size the
+  // partition length is chosen first, from the lengths: every item ends with a merge
+  // and, when split, partial results to write and merge later, which costs about as
+  // much per item whatever its length, so partitions are made as long as the load
+  // balance allows, a fixed fraction (kPartShare) of one workgroup's even share of all
+  // the (token, KV head tile) work, rounded down to 256 tokens, never below part_tokens.
+  // Every workgroup computes the same sum in the same order, so all choose alike.
+  // Then: the number of full partitions of each sequence and the class of its last one
+  // (0: an empty or invalid sequence, a one-item fill; 1: one chunk; 2 ..
+  // kSizeClasses - 1 by the last partition's size).
   {
-    int nfull1[4], nfull2[4], cls1[4], cls2[4], sum1 = 0, sum2 = 0;
-    auto size_class = [&](int L, int r, int pt) {
-      return L <= 32 ? 1
-                     : 2 + (int)min((int64_t)(kSizeClasses - 3),
-                                    ((int64_t)(r - 1) * (kSizeClasses - 2)) / pt);
-    };
+    int Ls[4];
+    float lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = 4 * tid + i;
-      nfull1[i] = nfull2[i] = cls1[i] = cls2[i] = 0;
+      Ls[i] = 0;
       if (s < S) {
         const int L = P.seq_lens[s];
         sm_len[s] = L;
-        if (L > 0 && L <= P.max_tokens) {
-          const int n1 = (L + PT - 1) / PT, n2 = (L + 2 * PT - 1) / (2 * PT);
-          nfull1[i] = n1 - 1;
-          nfull2[i] = n2 - 1;
-          cls1[i] = size_class(L, L - (n1 - 1) * PT, PT);  // r: tokens in the last partition
-          cls2[i] = size_class(L, L - (n2 - 1) * 2 * PT, 2 * PT);
-        }
+        if (L > 0 && L <= P.max_tokens) Ls[i] = L;
       }
-      sum1 += nfull1[i];
-      sum2 += nfull2[i];
+      lsum += (float)Ls[i];
     }
-    const int incl1 = wave_incl_scan(sum1, lane);
-    const int incl2 = wave_incl_scan(sum2, lane);
-    if (lane == 63) {
-      sm_wsum[wave] = incl1;
-      sm_wsum2[wave] = incl2;
-    }
-    __syncthreads();
-    int F1 = 0, F2 = 0;
+    if (P.auto_part) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      F1 += sm_wsum[w];
-      F2 += sm_wsum2[w];
+      for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
+      if (lane == 0) sm_wsumf[wave] = lsum;
+      __syncthreads();
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += sm_wsumf[w];
+      const float share = tot * (float)HT2 / (float)gridDim.x;  // tokens per workgroup
+      const float want = fminf(kPartShare * share, (float)P.max_tokens);
+      PT = max(PT, ((int)want / 256) * 256);
     }
-    const bool dbl = P.auto_part && (int64_t)F1 * HT2 >= 4 * (int64_t)gridDim.x;
-    int run = dbl ? incl2 - sum2 : incl1 - sum1;
-    for (int w = 0; w < wave; ++w) run += dbl ? sm_wsum2[w] : sm_wsum[w];
+    int nfull[4], cls[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int L = Ls[i];
+      nfull[i] = cls[i] = 0;
+      if (L > 0) {
+        const int n = (L + PT - 1) / PT;
+        const int r = L - (n - 1) * PT;  // tokens in the last partition, 1..PT
+        nfull[i] = n - 1;
+        cls[i] = L <= 32 ? 1
+                         : 2 + (int)min((int64_t)(kSizeClasses - 3),
+                                        ((int64_t)(r - 1) * (kSizeClasses - 2)) / PT);
+      }
+      sum += nfull[i];
+    }
+    const int incl = wave_incl_scan(sum, lane);
+    if (lane == 63) sm_wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += sm_wsum[w];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = 4 * tid + i;
       if (s < S) {
         sm_full[s] = run;
-        sm_class[s] = dbl ? cls2[i] : cls1[i];
+        sm_class[s] = cls[i];
       }
-      run += dbl ? nfull2[i] : nfull1[i];
+      run += nfull[i];
     }
     if (tid == 0) {
-      sm_full[S] = dbl ? F2 : F1;
-      sm_pt = dbl ? 2 * PT : PT;
+      int F = 0;
+      for (int w = 0; w < NW; ++w) F += sm_wsum[w];
+      sm_full[S] = F;
     }
   }
   __syncthreads();
-  PT = __builtin_amdgcn_readfirstlane(sm_pt);
+  PT = __builtin_amdgcn_readfirstlane(PT);
   // Stable counting sort of the sequences by size class, largest class first, and the
   // queue layout it gives: regular items (full partitions, then last partitions by
   // decreasing size), then one-chunk sequences NW items to a workgroup (one per wave),

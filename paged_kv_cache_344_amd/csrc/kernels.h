@@ -11,6 +11,7 @@ constexpr int kScanMax = 1024;      // sequences one decode launch plans for (ho
 constexpr int kMergeFan = 16;       // partials combined per merge node
 constexpr int kMaxPartitions = 8192;
 constexpr int kSizeClasses = 17;    // classes the last partitions are ordered by
+constexpr float kPartShare = 0.75f;  // default partition: this fraction of a workgroup's share
 
 // Everything a decode launch needs; passed by value as the kernel argument.  The
 // launch covers num_seqs sequences starting at the pointers given (the host slices
@@ -39,7 +40,7 @@ struct DecodeParams {
   int32_t max_blocks;           // row stride of block_tables
   int32_t max_tokens;           // max_blocks * bs
   int32_t part_tokens;          // tokens per partition, a multiple of 32
-  int32_t auto_part;            // 1: default size; the kernel may double part_tokens
+  int32_t auto_part;            // 1: default size; the kernel may lengthen part_tokens
   int32_t stream_kv;            // 1: no table shares a block: K/V loads are non-temporal
   int32_t pmax;                 // ceil(max_tokens / part_tokens)
   int32_t nodes;                // ceil(pmax / kMergeFan)
