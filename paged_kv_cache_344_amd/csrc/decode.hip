@@ -66,9 +66,10 @@
 // form groups of 16, and the item that completes a group (an arrival counter)
 // combines the group with log-sum-exp weights, and the item that completes the
 // last group combines the groups.  The group arrival's answer is read at the
-// workgroup's next item start, under that item's first loads.  The tree is fixed by partition numbers, so the
-// result does not depend on timing or on which workgroup ran what.  Counters are
-// reset by whoever finishes them, so they are all zero again after a call.
+// workgroup's next item start, under that item's first loads.  The tree is fixed by
+// partition numbers, so the result does not depend on timing or on which workgroup
+// ran what.  Counters are reset by whoever finishes them, so they are all zero again
+// after a call.
 #include <math.h>
 
 #include "decode_common.h"
