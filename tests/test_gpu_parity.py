@@ -297,16 +297,20 @@ def test_empty_bad_length_and_bad_block_rows():
 
 # ------------------------------------------------------------------ full-size batches
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("name", ["mha_fp16", "gqa_bf16", "prefix_bf16"])
-def test_full_size_parity(name):
-    b = inputs.make_batch(name, seed=0)
-    _parity(b, what=f"{name} full")
+def test_full_size_parity(name, seed):
+    """The benchmark batches at full size, default partitioning, on the three seeds of
+    the input recipe (seed 0 is the one measured)."""
+    b = inputs.make_batch(name, seed=seed)
+    _parity(b, what=f"{name} full seed {seed}")
 
 
-@pytest.mark.parametrize("name", ["long_bf16_bs16", "long_bf16_bs32"])
+@pytest.mark.parametrize("name", ["long_bf16_bs16", "long_bf16_bs32", "long_bf16_bs16_default"])
 def test_full_size_long_context_sampled(name):
-    """The long-context batch at full size in the benchmark's launch configuration
-    (512-token partitions); the oracle checks two of the eight sequences, every head."""
+    """The long-context batch at full size in the benchmark's launch configurations
+    (512-token partitions, and the default partitioning, which takes 6144-token
+    partitions on this batch); the oracle checks two of the eight sequences, every head."""
     b = inputs.make_batch(name, seed=0)
     g = OnGpu(b)
     got = g.out_f64(g.decode(b.partition_size))
