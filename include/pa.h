@@ -261,7 +261,7 @@ typedef struct pa_multi_token_ext {
  * unsplit result up to fp32 rounding.  partition_size > 0 fixes part_tokens; 0 picks
  * it from the shapes alone (rows per tile, table capacity max_blocks_per_seq * bs,
  * the number of triples): a split only when there are fewer than 512 triples and
- * partitions of at least max(256, 16 * rows per tile) tokens, and then about 2048
+ * partitions of at least max(256, 16 * rows per tile) tokens, and then about 768
  * workgroups.  The automatic choice assumes sequences near the table's capacity;
  * callers that know shorter lengths pass partition_size.
  *

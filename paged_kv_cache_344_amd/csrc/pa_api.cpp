@@ -196,13 +196,14 @@ pa_status plan_multi_token(const pa_multi_token_ext* ext, int32_t bs, int32_t hk
   if (psz > 0) {
     part_tokens = psz;
   } else if (psz == 0) {
-    // about 2048 workgroups (four rounds of the two per CU that fit, so that sequences
-    // shorter than the table's capacity, whose last partitions are empty, still leave
-    // enough), partitions long enough that their partials ((D + 2) * 4 bytes per row)
-    // stay small next to the K/V they replace (2 * D * 2 bytes per position): at least
-    // 16 positions per stored row
+    // about 768 workgroups (one and a half rounds of the two per CU that fit on a
+    // 256-CU device: fewer, longer partitions write and merge fewer partials, and
+    // measured on draft verification 704-832 workgroups beat both 576 and 1024-2048),
+    // partitions long enough that their partials ((D + 2) * 4 bytes per row) stay small
+    // next to the K/V they replace (2 * D * 2 bytes per position): at least 16
+    // positions per stored row
     const int64_t min_part = std::max<int64_t>(256, (16 * part_rows + 31) / 32 * 32);
-    const int64_t want = (2048 + triples - 1) / triples;
+    const int64_t want = (768 + triples - 1) / triples;
     const int64_t fit = max_tokens / min_part;
     const int64_t parts = std::min(want, fit);
     if (triples < 512 && parts >= 2) part_tokens = ((max_tokens + parts - 1) / parts + 31) / 32 * 32;

@@ -296,7 +296,7 @@ def _mt_expected(S, T, mq, Hq, Hkv, D, MB, bs, psz):
         return 0
     else:
         min_part = max(256, -(-16 * part_rows // 32) * 32)
-        parts = min(-(-2048 // triples), max_tokens // min_part)
+        parts = min(-(-768 // triples), max_tokens // min_part)
         if triples >= 512 or parts < 2:
             return 0
         pt = -(-(-(-max_tokens // parts)) // 32) * 32
@@ -332,10 +332,11 @@ def test_multi_token_workspace_formula(lib, kw):
 
 def test_multi_token_split_examples(lib):
     # 2 sequences x 8 KV heads x 4 tokens x G 8 = 32 rows: 16 triples, 32768 positions
-    # -> 128 wanted, 64 of the 512-position minimum fit: 64 partitions of 512,
-    # 16 * 64 * 32 rows of (128 + 2) floats
+    # -> 48 wanted (768 workgroups), 64 of the 512-position minimum fit: 48 partitions
+    # of ceil(32768 / 48) = 683 -> 704 positions, so 47 partitions;
+    # 16 * 47 * 32 rows of (128 + 2) floats
     st, n = _mt_ws(lib, num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=2048)
-    assert st == B.PA_OK and n == 16 * 64 * 32 * 130 * 4
+    assert st == B.PA_OK and n == 16 * 47 * 32 * 130 * 4
     st, n = _mt_ws(lib, num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=2048,
                    partition_size=96)
     assert st == B.PA_OK and n == 16 * 342 * 32 * 130 * 4
