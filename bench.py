@@ -498,7 +498,7 @@ def main():
                    "num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads,
                    "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
                    "block_size": b.block_size, "sum_L": tokens,
-                   "partition_size": b.partition_size or "default (768 tokens for this batch)",
+                   "partition_size": b.partition_size or "default (1024 tokens for this batch)",
                    "rotated_copies": head["n_copies"], "parallelism": "1 GPU"},
         "roofline": {"bound": "hbm", "achieved": head["gbps"], "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": head["gbps"] / PEAK_GBPS, "traffic": traffic,
