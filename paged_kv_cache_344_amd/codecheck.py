@@ -1,0 +1,111 @@
+"""Checks on the gfx950 machine code of libpa.so, run by build.build() after every
+build (the AMD assembly of our own code objects, disassembled with ROCm's llvm-objdump).
+
+1. No packed fp32 arithmetic (v_pk_add_f32, v_pk_mul_f32, v_pk_fma_f32).  The device
+   pass is compiled with the target feature that forbids them; this check makes sure
+   that stays true, whatever the compiler version.
+2. M0 is touched only by the multi-token kernel's global -> LDS loads.  Those loads are
+   inline assembly that sets M0 (the LDS destination) right before each load; the
+   compiler cannot keep a value of its own live in M0 across such a statement, so the
+   check requires that no compiler-generated instruction reads or writes M0 at all:
+   every instruction naming M0 must be `s_mov_b32 m0, sN` directly followed by
+   `s_nop 0` and a `global_load_lds_*`, every `global_load_lds_*` must come right after
+   such a pair, and no instruction that uses M0 implicitly (indexed register moves,
+   messages, GWS, LDS-append, other LDS-DMA forms) may appear.
+"""
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+import tempfile
+
+LLVM = "/opt/rocm/llvm/bin"
+TARGET = "hipv4-amdgcn-amd-amdhsa--gfx950"
+MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
+
+PACKED_FP32 = re.compile(r"\bv_pk_(add|mul|fma)_f32\b")
+NAMES_M0 = re.compile(r"\bm0\b")
+IMPLICIT_M0 = re.compile(r"\b(s_movrel\w*|v_movrel\w*|s_sendmsg\w*|ds_gws_\w+|ds_append|ds_consume|"
+                         r"ds_read_addtid\w*|ds_write_addtid\w*|buffer_load_\w+\s.*\blds\b|"
+                         r"buffer_store_lds\w*|s_set_gpr_idx_\w+)")
+
+
+def _tool(name: str) -> str:
+    p = os.path.join(LLVM, name)
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} not found (ROCm llvm tools are needed to check the code objects)")
+    return p
+
+
+def disassemble(lib_path: str) -> list:
+    """Disassembly text of every gfx950 code object bundled in lib_path (one per
+    translation unit)."""
+    with tempfile.TemporaryDirectory() as tmp:
+        fat = os.path.join(tmp, "fat.bin")
+        subprocess.run([_tool("llvm-objcopy"), f"--dump-section=.hip_fatbin={fat}", lib_path,
+                        os.path.join(tmp, "stripped")], check=True)
+        data = open(fat, "rb").read()
+        starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)]
+        out = []
+        for k, p in enumerate(starts):
+            end = starts[k + 1] if k + 1 < len(starts) else len(data)
+            bundle, co = os.path.join(tmp, f"b{k}.bin"), os.path.join(tmp, f"co{k}.o")
+            open(bundle, "wb").write(data[p:end])
+            subprocess.run([_tool("clang-offload-bundler"), "--unbundle", "--type=o",
+                            f"--targets={TARGET}", f"--input={bundle}", f"--output={co}"],
+                           check=True)
+            out.append(subprocess.run([_tool("llvm-objdump"), "-d", "--mcpu=gfx950", co],
+                                      check=True, capture_output=True, text=True).stdout)
+        if not out:
+            raise RuntimeError(f"{lib_path}: no offload bundle found")
+        return out
+
+
+def _instructions(text: str):
+    """(function, instruction text) pairs, comments and encodings dropped."""
+    fn = "?"
+    for line in text.splitlines():
+        m = re.match(r"^[0-9a-f]+ <(.*)>:", line)
+        if m:
+            fn = m.group(1)
+            continue
+        if not line.startswith("\t"):
+            continue
+        ins = line.split("//")[0].strip()
+        if ins:
+            yield fn, ins
+
+
+def problems(texts: list) -> list:
+    """Violations of the two rules above, as readable strings (empty: all good)."""
+    bad = []
+    for text in texts:
+        ins = list(_instructions(text))
+        for i, (fn, s) in enumerate(ins):
+            if PACKED_FP32.search(s):
+                bad.append(f"packed fp32 instruction in {fn}: {s}")
+            if IMPLICIT_M0.search(s):
+                bad.append(f"instruction that uses M0 implicitly in {fn}: {s}")
+            if s.startswith("global_load_lds"):
+                ok = (i >= 2 and re.fullmatch(r"s_mov_b32 m0, s\d+", ins[i - 2][1])
+                      and ins[i - 1][1] == "s_nop 0")
+                if not ok:
+                    bad.append(f"LDS-DMA load without its own M0 set-up in {fn}: {s}")
+            elif NAMES_M0.search(s):
+                ok = (re.fullmatch(r"s_mov_b32 m0, s\d+", s) and i + 2 < len(ins)
+                      and ins[i + 1][1] == "s_nop 0" and ins[i + 2][1].startswith("global_load_lds"))
+                if not ok:
+                    bad.append(f"M0 used outside an LDS-DMA load sequence in {fn}: {s}")
+    return bad
+
+
+def check(lib_path: str) -> dict:
+    """Raise RuntimeError listing every violation; return counts otherwise."""
+    texts = disassemble(lib_path)
+    bad = problems(texts)
+    if bad:
+        head = "\n  ".join(bad[:20])
+        raise RuntimeError(f"{lib_path}: {len(bad)} machine-code check failure(s):\n  {head}")
+    n_lds = sum(t.count("global_load_lds") for t in texts)
+    return {"code_objects": len(texts), "lds_dma_loads": n_lds}

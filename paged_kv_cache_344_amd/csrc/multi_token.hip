@@ -211,6 +211,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 // inline assembly so that the compiler's wait insertion, which cannot tell the chunk
 // buffers apart, does not wait for every load in flight before each LDS read; the waits
 // for these loads are the pipeline's own (wait_loads_and_sync).
+// Each statement sets M0 (the LDS destination) itself and lists it as clobbered.  The
+// compiler warns that it cannot save a reserved register around such a statement; it
+// never has to, because nothing else in the library's code reads or writes M0: every
+// build disassembles the code objects and fails if any instruction other than these
+// set-up + load sequences touches M0 (codecheck.py).
 // With NTL the load is non-temporal: for K/V that no other workgroup reads.
 template <int SIZE, bool NTL>
 __device__ __forceinline__ void load_to_lds(const void* g, const void* lds) {
