@@ -80,23 +80,28 @@ class BlockModel:
         del self.lengths[sid]
 
     # -- one new token for each listed sequence ----------------------------------
-    def _blocks_needed(self, sid: int) -> int:
-        if self.lengths[sid] % self.block_size == 0:
-            return 1                      # last block full, or no block yet
-        if self.refs[self.tables[sid][-1]] > 1:
-            return 1                      # shared and partly filled: copy first
-        return 0
-
     def append(self, seqs):
         """Returns (slot ids, [(source, destination) block copies]); raises
-        CapacityError and changes nothing if the pool or a table would overflow."""
+        CapacityError and changes nothing if the pool or a table would overflow.
+
+        Blocks needed: one for every sequence whose last block is full (or that has
+        none), and for every shared, partly filled last block X listed by k of its
+        holders, min(k, refs(X) - 1) copies: the holders are served in the order given,
+        each copy drops X's count by one, and once the last remaining holder is alone
+        on X it writes into X itself."""
         assert len(set(seqs)) == len(seqs), "each sequence at most once per step"
         need = 0
+        holders = {}                      # shared, partly filled last block -> listed holders
         for sid in seqs:
-            n = self._blocks_needed(sid)
-            if self.lengths[sid] % self.block_size == 0 and len(self.tables[sid]) + 1 > self.max_blocks:
-                raise CapacityError(f"sequence {sid} would need more than {self.max_blocks} blocks")
-            need += n
+            if self.lengths[sid] % self.block_size == 0:
+                if len(self.tables[sid]) + 1 > self.max_blocks:
+                    raise CapacityError(f"sequence {sid} would need more than {self.max_blocks} blocks")
+                need += 1
+            elif self.refs[self.tables[sid][-1]] > 1:
+                x = self.tables[sid][-1]
+                holders[x] = holders.get(x, 0) + 1
+        for x, k in holders.items():
+            need += min(k, self.refs[x] - 1)
         if need > len(self.free):
             raise CapacityError(f"{need} free blocks needed, {len(self.free)} free")
         slots, copies = [], []

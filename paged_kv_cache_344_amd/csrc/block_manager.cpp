@@ -163,18 +163,27 @@ pa_status pa_bm_append(pa_block_manager* bm, const int32_t* seqs, int32_t n,
   } catch (...) {
     return fail(PA_ERR_INVALID_ARG, "out of host memory");
   }
-  for (int32_t i = 0; i < n; ++i) {
-    const Sequence* s = bm->find(seqs[i]);
-    if (!s) return fail(PA_ERR_INVALID_ARG, "no sequence %d", seqs[i]);
-    const int32_t off = s->len % bm->block_size;
-    if (off == 0) {  // the last block is full (or there is none): take a new one
-      if ((int64_t)s->blocks.size() + 1 > bm->max_blocks)
-        return fail(PA_ERR_CAPACITY, "sequence %d would need more than %d blocks", seqs[i], bm->max_blocks);
-      ++need;
-    } else if (bm->refs[(size_t)s->blocks.back()] > 1) {  // shared, partly filled: copy first
-      ++need;
+  // A shared, partly filled last block X listed by k of its holders takes min(k,
+  // refs(X) - 1) copies: holders are served in the order given, each copy drops X's
+  // count by one, and the last holder left alone on X writes into it in place.
+  std::unordered_map<int32_t, int32_t> holders;
+  try {
+    for (int32_t i = 0; i < n; ++i) {
+      const Sequence* s = bm->find(seqs[i]);
+      if (!s) return fail(PA_ERR_INVALID_ARG, "no sequence %d", seqs[i]);
+      const int32_t off = s->len % bm->block_size;
+      if (off == 0) {  // the last block is full (or there is none): take a new one
+        if ((int64_t)s->blocks.size() + 1 > bm->max_blocks)
+          return fail(PA_ERR_CAPACITY, "sequence %d would need more than %d blocks", seqs[i], bm->max_blocks);
+        ++need;
+      } else if (bm->refs[(size_t)s->blocks.back()] > 1) {  // shared, partly filled: copy first
+        ++holders[s->blocks.back()];
+      }
     }
+  } catch (...) {
+    return fail(PA_ERR_INVALID_ARG, "out of host memory");
   }
+  for (const auto& h : holders) need += std::min<int64_t>(h.second, bm->refs[(size_t)h.first] - 1);
   if (need > (int64_t)bm->free_list.size())
     return fail(PA_ERR_CAPACITY, "%lld free blocks needed, %zu free", (long long)need,
                 bm->free_list.size());

@@ -86,6 +86,21 @@ def test_cpp_manager_worked_example():
     assert cm.free_blocks() == 13
 
 
+def test_cpp_siblings_appending_together_copy_all_but_one():
+    """As the model: holders of one shared, partly filled block appending together need
+    refs - 1 free blocks, the last listed holder writing in place."""
+    cm = B.BlockManager(3, 4, 4)
+    a = cm.add_sequence()
+    for _ in range(6):
+        cm.append([a])
+    b = cm.fork(a)
+    slots, copies = cm.append([a, b])
+    assert copies == [(1, 2)] and slots == [2 * 4 + 2, 1 * 4 + 2]
+    bt, sl = cm.export([a, b])
+    assert bt[:, :2].tolist() == [[0, 2], [0, 1]] and sl.tolist() == [7, 7]
+    assert [cm.ref_count(x) for x in range(3)] == [2, 1, 1] and cm.free_blocks() == 0
+
+
 def test_cpp_manager_rejects():
     with pytest.raises(B.PaError):
         B.BlockManager(0, 4, 4)

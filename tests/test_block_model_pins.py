@@ -97,6 +97,38 @@ def test_model_copy_on_write_of_a_partly_filled_shared_block():
     assert copies == [] and slots == [1 * 4 + 2]
 
 
+def test_model_siblings_appending_together_copy_all_but_one():
+    """Holders of one shared, partly filled block appending in the same call: all but
+    the last listed copy it, and the last, then alone on it, writes in place -- so the
+    call needs refs - 1 free blocks, not one per holder."""
+    m = model.BlockModel(3, 4, 4)
+    a = m.add_sequence()
+    for _ in range(6):                # blocks 0 (full) and 1 (2 of 4); block 2 free
+        m.append([a])
+    b = m.fork(a)
+    slots, copies = m.append([a, b])  # one free block is enough
+    assert copies == [(1, 2)]
+    assert slots == [2 * 4 + 2, 1 * 4 + 2]
+    assert m.tables[a] == [0, 2] and m.tables[b] == [0, 1]
+    assert m.refs == [2, 1, 1] and m.free_blocks() == 0
+    # three holders of block 1: two copies; with one free block the call fails untouched
+    m = model.BlockModel(4, 4, 4)
+    a = m.add_sequence()
+    for _ in range(6):
+        m.append([a])
+    b, c = m.fork(a), m.fork(a)
+    m.add_sequence()
+    d = m.add_sequence()
+    m.append([d])                     # takes block 2: one free block left
+    with pytest.raises(model.CapacityError):
+        m.append([c, a, b])
+    assert m.refs[1] == 3 and m.free_blocks() == 1 and m.lengths[a] == 6
+    m.free_sequence(d)                # two free blocks
+    slots, copies = m.append([c, a, b])
+    assert [s for s, _ in copies] == [1, 1] and m.refs[1] == 1
+    assert m.tables[b] == [0, 1] and slots[2] == 1 * 4 + 2
+
+
 def test_model_frees_at_zero_and_fifo_reuse():
     m = model.BlockModel(4, 2, 4)
     a = m.add_sequence()
