@@ -134,10 +134,28 @@ def _check(status: int, where: str):
         raise PaError(status, where, L.pa_last_error().decode() or L.pa_status_string(status).decode())
 
 
-def _stream_ptr(device: torch.device, stream) -> Optional[int]:
+def _torch_stream(device: torch.device, stream):
+    """The stream a call runs on, as a torch stream object: the current one when None, a
+    torch stream as given, or a raw hipStream_t (int) wrapped as an external stream."""
     if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _stream_ptr(device: torch.device, stream) -> Optional[int]:
+    return _torch_stream(device, stream).cuda_stream
+
+
+def _scratch_on(stream_obj, nbytes: int, zero: bool) -> torch.Tensor:
+    """A byte tensor allocated (and zero-filled when asked) on the stream the call runs on,
+    so that torch's caching allocator orders any later reuse of its memory after the
+    call's kernels, even when the tensor is dropped right after the call returns."""
+    with torch.cuda.stream(stream_obj):
+        if zero:
+            return torch.zeros(nbytes, dtype=torch.uint8, device=stream_obj.device)
+        return torch.empty(nbytes, dtype=torch.uint8, device=stream_obj.device)
 
 
 def _need(cond: bool, msg: str):
@@ -207,14 +225,16 @@ class PreparedDecode:
         need = ctypes.c_size_t(0)
         _check(lib().pa_decode_workspace_bytes(ctypes.byref(ext), block_size, num_kv_heads,
                                                ctypes.byref(need)), "pa_decode")
+        ts = _torch_stream(dev, stream)
         if workspace is None:
-            # zero-filled, as the library requires before a workspace's first use;
-            # every call returns its counters to zero
-            workspace = torch.zeros(need.value, dtype=torch.uint8, device=dev)
+            # zero-filled, as the library requires before a workspace's first use (every
+            # call returns its counters to zero); allocated and cleared on the launch
+            # stream, so its memory is not handed out again before the kernel is done
+            workspace = _scratch_on(ts, need.value, zero=True)
         _need(workspace.device == dev and workspace.is_contiguous(), "workspace placement")
         ext.workspace = workspace.data_ptr()
         ext.workspace_bytes = workspace.numel() * workspace.element_size()
-        ext.stream = _stream_ptr(dev, stream)
+        ext.stream = ts.cuda_stream
         ext.shared_blocks = 1 if shared_blocks else 0
         self.ext = ext
         self.tensors = (q, k_cache, v_cache, block_tables, seq_lens, out, workspace)
@@ -331,13 +351,14 @@ class PreparedMultiToken:
         _check(lib().pa_multi_token_workspace_bytes(ctypes.byref(ext), block_size, num_kv_heads,
                                                     ctypes.byref(need)), "pa_multi_token")
         self.workspace_bytes = need.value
+        ts = _torch_stream(dev, stream)
         if workspace is None and need.value:
-            workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)  # scratch
+            workspace = _scratch_on(ts, need.value, zero=False)  # scratch, on the launch stream
         if workspace is not None:
             _need(workspace.device == dev and workspace.is_contiguous(), "workspace placement")
             ext.workspace = workspace.data_ptr()
             ext.workspace_bytes = workspace.numel() * workspace.element_size()
-        ext.stream = _stream_ptr(dev, stream)
+        ext.stream = ts.cuda_stream
         self.ext = ext
         self.tensors = (q, k_cache, v_cache, block_tables, seq_lens, query_start, out, workspace)
         self.out = out
