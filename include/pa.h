@@ -146,7 +146,10 @@ typedef struct pa_decode_ext {
  * shape may leave partial results where this shape keeps counters: zero-fill the
  * workspace again before using it for a different shape (or keep one workspace per
  * shape).  Calls that share a workspace must be ordered on one stream: calls that
- * overlap on the same workspace race.
+ * overlap on the same workspace race.  Bytes 64..67 of the workspace (an int32) are not
+ * a counter: after a call they hold the partition length, in tokens, that it used (the
+ * default one chosen on the device, or partition_size; with more than 1024 sequences,
+ * that of the last launch of 1024).
  *
  * Execution: one persistent launch per 1024 sequences (about as many workgroups
  * as are resident on the device at once), each planning from seq_lens which

@@ -6,4 +6,4 @@ loudly when it has not been built."""
 from .binding import (BlockManager, PaError, PreparedCacheWrite,  # noqa: F401
                       PreparedCopyBlocks, PreparedDecode, PreparedMultiToken, pa_cache_write,
                       pa_copy_blocks, pa_decode, pa_decode_workspace_bytes, pa_multi_token,
-                      workspace_for)
+                      decode_partition_used, workspace_for)

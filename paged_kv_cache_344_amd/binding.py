@@ -250,6 +250,20 @@ class PreparedDecode:
             _check(st, "pa_decode")
         return self.out
 
+    def partition_used(self) -> int:
+        """Tokens per split-K partition that the last call used (waits for it)."""
+        return decode_partition_used(self.tensors[-1])
+
+
+PART_SLOT_BYTE = 64  # workspace bytes 64..67: the partition length the last call used
+
+
+def decode_partition_used(workspace: torch.Tensor) -> int:
+    """The partition length (tokens) recorded in a decode workspace by the last call that
+    used it; synchronises the device."""
+    torch.cuda.synchronize(workspace.device)
+    return int(workspace[PART_SLOT_BYTE:PART_SLOT_BYTE + 4].cpu().view(torch.int32).item())
+
 
 def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,

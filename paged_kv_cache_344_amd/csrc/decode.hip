@@ -245,6 +245,8 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   }
   __syncthreads();
   PT = __builtin_amdgcn_readfirstlane(PT);
+  // the partition length this launch uses, for the caller to read back (not a counter)
+  if (blockIdx.x == 0 && tid == 0) P.queue[kPartSlot] = PT;
   // Stable counting sort of the sequences by size class, largest class first, and the
   // queue layout it gives: regular items (full partitions, then last partitions by
   // decreasing size), then one-chunk sequences NW items to a workgroup (one per wave),

@@ -12,6 +12,8 @@ constexpr int kMergeFan = 16;       // partials combined per merge node
 constexpr int kMaxPartitions = 8192;
 constexpr int kSizeClasses = 17;    // classes the last partitions are ordered by
 constexpr float kPartShare = 0.75f;  // default partition: this fraction of a workgroup's share
+constexpr int kPartSlot = 16;       // int32 slot of the decode workspace header (byte 64) that
+                                    // records the partition length the last launch used
 
 // Everything a decode launch needs; passed by value as the kernel argument.  The
 // launch covers num_seqs sequences starting at the pointers given (the host slices
@@ -28,7 +30,8 @@ struct DecodeParams {
   float* part_ml;               // [S][pmax][Hq][2]   (running max in log2 units, sum)
   float* node_o;                // [S][nodes][Hq][D]  merged groups of kMergeFan partitions
   float* node_ml;               // [S][nodes][Hq][2]
-  int32_t* queue;               // [2]: next work item, finished workgroups (0 between calls)
+  int32_t* queue;               // [2]: next work item, finished workgroups (0 between calls);
+                                // [kPartSlot]: the partition length the launch used
   int32_t* node_count;          // [S][Hkv*tiles][nodes]: partitions finished per group
   int32_t* root_count;          // [S][Hkv*tiles]: groups finished per sequence and head tile
   int64_t num_blocks;           // N
