@@ -162,6 +162,29 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     int32_t num_kv_heads, float scale, void* out, const pa_decode_ext* ext);
 
 /*
+ * pa_decode_noalloc - pa_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops and harnesses that forbid allocation).
+ *
+ * Same arguments, results and errors as pa_decode, except that ext->workspace and
+ * ext->workspace_bytes are ignored: the call uses a scratch array that the library
+ * holds in device memory, PA_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU it runs on,
+ * from that GPU's first such call until the process ends.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine); it clears the scratch's counters with a
+ * small kernel on ext->stream, then launches the decode kernel there.  A call whose
+ * shapes need more scratch than that (see pa_decode_workspace_bytes) returns
+ * PA_ERR_WORKSPACE and launches nothing.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (on different streams, or from several host
+ * threads without ordering) race and give wrong results; calls ordered on one stream
+ * are safe.  The partition length a call used is not reported.
+ */
+pa_status pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            int32_t block_size, int32_t num_kv_heads, float scale, void* out,
+                            const pa_decode_ext* ext);
+
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
  * pa_decode_workspace_bytes - bytes of workspace a pa_decode call with these
  * shapes needs (always > 0: a few hundred bytes of counters when no sequence can
  * span two partitions, plus S * Hq * pmax * (D + 2) * 4 bytes of partials when

@@ -72,6 +72,8 @@ def lib():
         L.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp,
                                 ctypes.POINTER(DecodeExt)]
         L.pa_decode.restype = ctypes.c_int
+        L.pa_decode_noalloc.argtypes = L.pa_decode.argtypes
+        L.pa_decode_noalloc.restype = ctypes.c_int
         L.pa_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeExt), i32, i32,
                                                 ctypes.POINTER(ctypes.c_size_t)]
         L.pa_decode_workspace_bytes.restype = ctypes.c_int
@@ -200,7 +202,7 @@ class PreparedDecode:
                  block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
                  num_kv_heads: int, scale: float, out: torch.Tensor, *,
                  workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
-                 shared_blocks: bool = False, stream=None):
+                 shared_blocks: bool = False, stream=None, noalloc: bool = False):
         dev = q.device
         _need(dev.type == "cuda", "tensors must be on a GPU")
         for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
@@ -226,20 +228,25 @@ class PreparedDecode:
         _check(lib().pa_decode_workspace_bytes(ctypes.byref(ext), block_size, num_kv_heads,
                                                ctypes.byref(need)), "pa_decode")
         ts = _torch_stream(dev, stream)
-        if workspace is None:
-            # zero-filled, as the library requires before a workspace's first use (every
-            # call returns its counters to zero); allocated and cleared on the launch
-            # stream, so its memory is not handed out again before the kernel is done
-            workspace = _scratch_on(ts, need.value, zero=True)
-        _need(workspace.device == dev and workspace.is_contiguous(), "workspace placement")
-        ext.workspace = workspace.data_ptr()
-        ext.workspace_bytes = workspace.numel() * workspace.element_size()
+        if noalloc:
+            _need(workspace is None, "a no-allocation call takes no workspace")
+        else:
+            if workspace is None:
+                # zero-filled, as the library requires before a workspace's first use
+                # (every call returns its counters to zero); allocated and cleared on the
+                # launch stream, so its memory is not handed out again before the kernel
+                # is done
+                workspace = _scratch_on(ts, need.value, zero=True)
+            _need(workspace.device == dev and workspace.is_contiguous(), "workspace placement")
+            ext.workspace = workspace.data_ptr()
+            ext.workspace_bytes = workspace.numel() * workspace.element_size()
         ext.stream = ts.cuda_stream
         ext.shared_blocks = 1 if shared_blocks else 0
         self.ext = ext
         self.tensors = (q, k_cache, v_cache, block_tables, seq_lens, out, workspace)
         self.out = out
-        self._fn = lib().pa_decode
+        self._where = "pa_decode_noalloc" if noalloc else "pa_decode"
+        self._fn = lib().pa_decode_noalloc if noalloc else lib().pa_decode
         self._args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                       block_tables.data_ptr(), seq_lens.data_ptr(), block_size, num_kv_heads,
                       ctypes.c_float(scale), out.data_ptr(), ctypes.byref(ext))
@@ -247,11 +254,12 @@ class PreparedDecode:
     def __call__(self) -> torch.Tensor:
         st = self._fn(*self._args)
         if st != PA_OK:
-            _check(st, "pa_decode")
+            _check(st, self._where)
         return self.out
 
     def partition_used(self) -> int:
         """Tokens per split-K partition that the last call used (waits for it)."""
+        _need(self.tensors[-1] is not None, "a no-allocation call keeps no workspace to read")
         return decode_partition_used(self.tensors[-1])
 
 
@@ -284,6 +292,19 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                           num_kv_heads, scale, out, workspace=workspace,
                           partition_size=partition_size, shared_blocks=shared_blocks,
                           stream=stream)()
+
+
+def pa_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
+                      num_kv_heads: int, scale: float, out: torch.Tensor, *,
+                      partition_size: int = 0, shared_blocks: bool = False,
+                      stream=None) -> torch.Tensor:
+    """pa_decode without a workspace: the library's per-GPU static scratch serves the call
+    (see include/pa.h, pa_decode_noalloc); nothing is allocated here either."""
+    call = PreparedDecode(q, k_cache, v_cache, block_tables, seq_lens, block_size,
+                          num_kv_heads, scale, out, partition_size=partition_size,
+                          shared_blocks=shared_blocks, stream=stream, noalloc=True)
+    return call()
 
 
 class PreparedCacheWrite:

@@ -14,8 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libpa.so")
-SOURCES = ["decode.hip", "cache_write.hip", "copy_blocks.hip", "multi_token.hip", "pa_api.cpp",
-           "block_manager.cpp"]
+SOURCES = ["decode.hip", "cache_write.hip", "copy_blocks.hip", "multi_token.hip", "noalloc.hip",
+           "pa_api.cpp", "block_manager.cpp"]
 
 
 def hipcc() -> str:

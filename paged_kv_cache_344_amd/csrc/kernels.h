@@ -12,6 +12,7 @@ constexpr int kMergeFan = 16;       // partials combined per merge node
 constexpr int kMaxPartitions = 8192;
 constexpr int kSizeClasses = 17;    // classes the last partitions are ordered by
 constexpr float kPartShare = 0.75f;  // default partition: this fraction of a workgroup's share
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;  // pa_decode_noalloc's device scratch
 constexpr int kPartSlot = 16;       // int32 slot of the decode workspace header (byte 64) that
                                     // records the partition length the last launch used
 
@@ -115,5 +116,11 @@ hipError_t launch_multi_token(int dtype, int head_dim, int block_size, MultiToke
 // The log-sum-exp combination of a split launch's partitions into out.
 hipError_t launch_multi_token_merge(int dtype, int head_dim, const MultiTokenParams& p,
                                     hipStream_t stream);
+
+// pa_decode_noalloc: the device address of this device's static scratch array
+// (kStaticScratchBytes, 256-byte aligned), looked up once per device.
+hipError_t static_scratch(void** ptr);
+// Zero bytes (a multiple of 16) at p, 16-byte aligned, on stream.
+hipError_t launch_clear(void* p, size_t bytes, hipStream_t stream);
 
 }  // namespace pa

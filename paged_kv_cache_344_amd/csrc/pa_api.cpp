@@ -18,6 +18,9 @@
 #include "kernels.h"
 #include "pa.h"
 
+static_assert(PA_NOALLOC_SCRATCH_BYTES == pa::kStaticScratchBytes,
+              "pa.h and the library disagree on the no-allocation scratch size");
+
 namespace {
 
 thread_local std::string g_error;
@@ -241,14 +244,14 @@ pa_status pa_decode_workspace_bytes(const pa_decode_ext* ext, int32_t block_size
   return PA_OK;
 }
 
-pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, const int32_t* seq_lens, int32_t block_size,
-                    int32_t num_kv_heads, float scale, void* out, const pa_decode_ext* ext) {
-  g_error.clear();
-  Plan pl;
-  pa_status st = plan_decode(ext, block_size, num_kv_heads, &pl);
-  if (st != PA_OK) return st;
-  if (ext->num_seqs == 0) return PA_OK;
+}  // extern "C"
+
+namespace {
+
+// Checks of a decode call's tensor arguments (the workspace is checked by the callers).
+pa_status check_decode_args(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                            const void* out) {
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
     return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
@@ -256,17 +259,21 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (!aligned(block_tables, 4) || !aligned(seq_lens, 4))
     return fail(PA_ERR_INVALID_ARG, "block_tables and seq_lens must be 4-byte aligned");
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-  if (!ext->workspace || ext->workspace_bytes < pl.ws_bytes)
-    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.ws_bytes,
-                ext->workspace ? ext->workspace_bytes : (size_t)0);
-  if (!aligned(ext->workspace, 16)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return PA_OK;
+}
+
+// The decode launches of a checked call, with ws (of at least pl.ws_bytes bytes) as the
+// workspace.
+pa_status decode_launches(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens, int32_t block_size,
+                          int32_t num_kv_heads, float scale, void* out, const pa_decode_ext* ext,
+                          const Plan& pl, char* ws) {
   int grid = 0;
-  st = decode_grid(ext->dtype, ext->head_dim, block_size, &grid);
+  pa_status st = decode_grid(ext->dtype, ext->head_dim, block_size, &grid);
   if (st != PA_OK) return st;
 
   const int32_t S = ext->num_seqs, Hq = ext->num_q_heads, D = ext->head_dim;
   const int64_t ht2 = (int64_t)num_kv_heads * pl.head_tiles;
-  char* ws = static_cast<char*>(ext->workspace);
   pa::DecodeParams p;
   p.num_blocks = ext->num_blocks;
   p.num_q_heads = Hq;
@@ -312,6 +319,52 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
     if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   }
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens, int32_t block_size,
+                    int32_t num_kv_heads, float scale, void* out, const pa_decode_ext* ext) {
+  g_error.clear();
+  Plan pl;
+  pa_status st = plan_decode(ext, block_size, num_kv_heads, &pl);
+  if (st != PA_OK) return st;
+  if (ext->num_seqs == 0) return PA_OK;
+  st = check_decode_args(q, k_cache, v_cache, block_tables, seq_lens, scale, out);
+  if (st != PA_OK) return st;
+  if (!ext->workspace || ext->workspace_bytes < pl.ws_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.ws_bytes,
+                ext->workspace ? ext->workspace_bytes : (size_t)0);
+  if (!aligned(ext->workspace, 16)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return decode_launches(q, k_cache, v_cache, block_tables, seq_lens, block_size, num_kv_heads,
+                         scale, out, ext, pl, static_cast<char*>(ext->workspace));
+}
+
+pa_status pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            int32_t block_size, int32_t num_kv_heads, float scale, void* out,
+                            const pa_decode_ext* ext) {
+  g_error.clear();
+  Plan pl;
+  pa_status st = plan_decode(ext, block_size, num_kv_heads, &pl);
+  if (st != PA_OK) return st;
+  if (ext->num_seqs == 0) return PA_OK;
+  st = check_decode_args(q, k_cache, v_cache, block_tables, seq_lens, scale, out);
+  if (st != PA_OK) return st;
+  if (pl.ws_bytes > pa::kStaticScratchBytes)
+    return fail(PA_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use pa_decode with a workspace)", pl.ws_bytes, pa::kStaticScratchBytes);
+  void* ws = nullptr;
+  hipError_t e = pa::static_scratch(&ws);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "static scratch address: %s", hipGetErrorString(e));
+  // the array keeps the previous call's contents: its queue and merge counters start at zero
+  e = pa::launch_clear(ws, pl.off_part_o, static_cast<hipStream_t>(ext->stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "scratch clear launch: %s", hipGetErrorString(e));
+  return decode_launches(q, k_cache, v_cache, block_tables, seq_lens, block_size, num_kv_heads,
+                         scale, out, ext, pl, static_cast<char*>(ws));
 }
 
 pa_status pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
