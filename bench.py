@@ -2,7 +2,8 @@
 """Benchmark of the paged decode hot path on one MI355X.
 
 One step = one decode step of a batch: ``pa_cache_write`` of the batch's new tokens
-(one per sequence) followed by ``pa_decode`` over every sequence.  The headline batch
+(one per sequence) followed by ``pa_decode`` over every sequence (the same step as one
+``pa_cache_write_decode`` launch is reported beside it).  The headline batch
 is the bf16 GQA-8 batch (128 sequences, 64 query / 8 KV heads, head dim 128, block
 size 16, log-uniform lengths in [1, 4096], seed 0).  Inputs are resident in HBM before
 timing starts; several copies of the batch are rotated so that no step finds its K/V
@@ -46,7 +47,7 @@ HEADLINE = "gqa_bf16"
 WORKLOAD_TEXT = {
     "gqa_bf16": "bf16 GQA decode step: 128 seqs, 64 q heads / 8 KV heads, head_dim 128, "
                 "block_size 16, log-uniform lengths in [1, 4096], shuffled pool (+10% free); "
-                "pa_cache_write of 128 new tokens, then pa_decode",
+                "pa_cache_write of the 128 new tokens, then pa_decode",
     "long_bf16_bs16": "bf16 long-context split-K decode: 8 seqs, lengths uniform in "
                       "[32768, 131072], 32 q / 8 KV heads, head_dim 128, block_size 16, "
                       "512-token partitions",
@@ -181,29 +182,44 @@ class Copy:
             self.kn, self.vn = t(b.k_new), t(b.v_new)
             self.sm = torch.from_numpy(b.slot_mapping).to(dev)
             self.write = pa.PreparedCacheWrite(self.kn, self.vn, self.sm, self.kc, self.vc)
+            # the same step in one launch: new tokens stored, then decode
+            self.step = pa.PreparedDecode(self.q, self.kc, self.vc, self.bt, self.sl,
+                                          b.block_size, b.num_kv_heads, b.scale, self.out,
+                                          partition_size=partition_size,
+                                          shared_blocks=b.shared_blocks > 0,
+                                          new_tokens=(self.kn, self.vn, self.sm))
 
 
-def time_steps(copies, steps, warmup, with_write):
-    """Run warmup + timed steps rotating over copies; returns (elapsed_s, [decode_ms])."""
+def time_steps(copies, steps, warmup, with_write, fused=False):
+    """Run warmup + timed steps rotating over copies; returns (elapsed_s, [call_ms]).
+    A step is the decode call, preceded by the batch's cache write when with_write; with
+    fused, write and decode are the one pa_cache_write_decode call.  The events bracket
+    the decode call (the fused call when fused)."""
     import torch
     n = len(copies)
+
+    def run(c, ev=None):
+        if fused and with_write and c.write:
+            if ev:
+                ev[0].record()
+            c.step()
+        else:
+            if with_write and c.write:
+                c.write()
+            if ev:
+                ev[0].record()
+            c.decode()
+        if ev:
+            ev[1].record()
     for k in range(warmup):
-        c = copies[k % n]
-        if with_write and c.write:
-            c.write()
-        c.decode()
+        run(copies[k % n])
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
-        c = copies[k % n]
-        if with_write and c.write:
-            c.write()
-        ev[k][0].record()
-        c.decode()
-        ev[k][1].record()
+        run(copies[k % n], ev[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     return elapsed, [a.elapsed_time(z) for a, z in ev]
@@ -385,7 +401,7 @@ def measured_traffic(kernel_key, launches_bytes):
     return ent.get("bytes_per_call")
 
 
-def measure(name, seed, steps, warmup, copies_min, with_write):
+def measure(name, seed, steps, warmup, copies_min, with_write, fused=False):
     import torch
     from paged_kv_cache_344_amd import inputs
     t = time.perf_counter()
@@ -397,8 +413,10 @@ def measure(name, seed, steps, warmup, copies_min, with_write):
     part = b.partition_size
     copies = [Copy(b, part) for _ in range(n_copies)]
     torch.cuda.synchronize()
-    elapsed, dms = time_steps(copies, steps, warmup, with_write)
+    elapsed, dms = time_steps(copies, steps, warmup, with_write, fused)
     dec_bytes = decode_bytes(b)
+    if fused and b.slot_mapping is not None:  # the timed call also stores the new tokens
+        dec_bytes += cache_write_bytes(b)
     mean_ms = sum(dms) / len(dms)
     srt = sorted(dms)
     if b.query_start is not None:
@@ -458,6 +476,16 @@ def main():
     b = head["batch"]
     tokens = b.total_tokens()
     value = args.steps * tokens / head["elapsed"]
+
+    # the same step in one launch, pa_cache_write_decode (same copies), for context
+    el2, dms2 = time_steps(head["copies"], args.steps, args.warmup, with_write=True, fused=True)
+    fused = {"value": args.steps * tokens / el2, "unit": "tokens/s",
+             "ms_per_step": el2 / args.steps * 1e3,
+             "call_us": sum(dms2) / len(dms2) * 1e3,
+             "what": "pa_cache_write_decode: the new tokens stored and every sequence "
+                     "decoded in one launch"}
+    log(f"{HEADLINE} as one fused call: {fused['ms_per_step'] * 1e3:.1f} us per step, call "
+        f"{fused['call_us']:.1f} us")
 
     # the cache write of the headline step alone (same copies, same slots each time)
     cw = summary_us(time_calls([c.write for c in head["copies"]], max(50, args.steps // 2)))
@@ -561,6 +589,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": par,
         "step_bytes": head["decode_bytes"] + head["write_bytes"],
+        "fused_step": fused,
         "cache_write": cw,
         "tiny_fp32": tiny,
         "also": also,

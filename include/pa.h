@@ -162,6 +162,35 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     int32_t num_kv_heads, float scale, void* out, const pa_decode_ext* ext);
 
 /*
+ * pa_cache_write_decode - one decode step in one launch: pa_cache_write of each
+ * sequence's new token, then pa_decode, with the same results, bit for bit, as those two
+ * calls in that order on one stream ([RK] 分页注意力是如何工作的: each step stores the new
+ * token in the next slot of its sequence's last block and attends over all tokens so
+ * far).
+ *
+ *   k, v          [S][Hkv][D]   dtype, device: row s is sequence s's new token
+ *   slot_mapping  [S]           int64, device: its slot (< 0: sequence s has none)
+ *   q ... out, ext              as for pa_decode (the same workspace rules)
+ *
+ * Contract, beyond the two calls': slot_mapping[s], when >= 0, is the slot of position
+ * seq_lens[s] - 1 of sequence s (the slot the decode then reads the new token from), and
+ * no block table reads a slot that another sequence's token is written to (a block
+ * several tables share is copied first, [CY] 多序列共享).  Inside the launch the stores of
+ * the new tokens and the reads of the cache are not ordered; the decode takes sequence
+ * s's last key and value from k and v instead of the cache when slot_mapping[s] is that
+ * position's slot (checked per sequence on the device).  If slot_mapping[s] names another
+ * slot, the token is still stored there and the decode reads position seq_lens[s] - 1
+ * from the cache as it stands; a slot both written and read in one call gives an
+ * undefined value.  Errors: those of pa_decode, and PA_ERR_INVALID_ARG for NULL or
+ * misaligned k, v (16 bytes) or slot_mapping (8 bytes).
+ */
+pa_status pa_cache_write_decode(const void* k, const void* v, const int64_t* slot_mapping,
+                                const void* q, void* k_cache, void* v_cache,
+                                const int32_t* block_tables, const int32_t* seq_lens,
+                                int32_t block_size, int32_t num_kv_heads, float scale, void* out,
+                                const pa_decode_ext* ext);
+
+/*
  * pa_decode_noalloc - pa_decode for callers that cannot allocate device memory (code
  * under HIP graph capture, serving loops and harnesses that forbid allocation).
  *
@@ -365,7 +394,7 @@ const char* pa_last_error(void);
 /* ABI version of this header: bumped on any incompatible change. */
 int32_t pa_abi_version(void);
 
-#define PA_ABI_VERSION 2  /* 2: pa_decode_ext.shared_blocks */
+#define PA_ABI_VERSION 3  /* 2: pa_decode_ext.shared_blocks; 3: pa_cache_write_decode */
 
 #ifdef __cplusplus
 }

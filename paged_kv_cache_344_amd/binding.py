@@ -16,7 +16,7 @@ from .build import LIB_PATH, INCLUDE
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_CAPACITY = range(6)
 PA_F32, PA_F16, PA_BF16 = range(3)
-ABI_VERSION = 2  # PA_ABI_VERSION of the header these structures mirror
+ABI_VERSION = 3  # PA_ABI_VERSION of the header these structures mirror
 TORCH_DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
 
@@ -72,6 +72,9 @@ def lib():
         L.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp,
                                 ctypes.POINTER(DecodeExt)]
         L.pa_decode.restype = ctypes.c_int
+        L.pa_cache_write_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                            ctypes.c_float, vp, ctypes.POINTER(DecodeExt)]
+        L.pa_cache_write_decode.restype = ctypes.c_int
         L.pa_decode_noalloc.argtypes = L.pa_decode.argtypes
         L.pa_decode_noalloc.restype = ctypes.c_int
         L.pa_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeExt), i32, i32,
@@ -202,7 +205,8 @@ class PreparedDecode:
                  block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
                  num_kv_heads: int, scale: float, out: torch.Tensor, *,
                  workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
-                 shared_blocks: bool = False, stream=None, noalloc: bool = False):
+                 shared_blocks: bool = False, stream=None, noalloc: bool = False,
+                 new_tokens=None):
         dev = q.device
         _need(dev.type == "cuda", "tensors must be on a GPU")
         for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
@@ -250,6 +254,23 @@ class PreparedDecode:
         self._args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                       block_tables.data_ptr(), seq_lens.data_ptr(), block_size, num_kv_heads,
                       ctypes.c_float(scale), out.data_ptr(), ctypes.byref(ext))
+        if new_tokens is not None:
+            # one launch: each sequence's new token is stored, then decoded over
+            _need(not noalloc, "the fused write + decode takes a workspace")
+            k, v, slot_mapping = new_tokens
+            for name, t in (("k", k), ("v", v), ("slot_mapping", slot_mapping)):
+                _need(t.device == dev and t.is_contiguous(), f"{name} placement")
+            _need(k.dtype == q.dtype and v.dtype == q.dtype, "k and v must have q's dtype")
+            _need(k.shape == (S, num_kv_heads, D) and v.shape == k.shape, "k / v shape")
+            _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (S,),
+                  "slot_mapping must be int64 [S]")
+            self._where = "pa_cache_write_decode"
+            self._fn = lib().pa_cache_write_decode
+            self._args = (k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr()) + (
+                q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                seq_lens.data_ptr(), block_size, num_kv_heads, ctypes.c_float(scale),
+                out.data_ptr(), ctypes.byref(ext))
+            self.new_tokens = (k, v, slot_mapping)
 
     def __call__(self) -> torch.Tensor:
         st = self._fn(*self._args)
@@ -292,6 +313,21 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                           num_kv_heads, scale, out, workspace=workspace,
                           partition_size=partition_size, shared_blocks=shared_blocks,
                           stream=stream)()
+
+
+def pa_cache_write_decode(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                          q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
+                          num_kv_heads: int, scale: float, out: torch.Tensor, *,
+                          workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
+                          shared_blocks: bool = False, stream=None) -> torch.Tensor:
+    """One decode step in one launch (see include/pa.h): each sequence's new token (row s
+    of k, v [S, Hkv, D]) is stored in slot_mapping[s] (int64 [S]), then every sequence is
+    decoded; the same bits as pa_cache_write followed by pa_decode."""
+    return PreparedDecode(q, k_cache, v_cache, block_tables, seq_lens, block_size,
+                          num_kv_heads, scale, out, workspace=workspace,
+                          partition_size=partition_size, shared_blocks=shared_blocks,
+                          stream=stream, new_tokens=(k, v, slot_mapping))()
 
 
 def pa_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -79,6 +79,8 @@ namespace {
 
 using namespace dec;
 
+constexpr int kWriteRows = 16;  // (token, KV head) rows a workgroup stores per claim (fused write)
+
 // Log-sum-exp combination of cnt partials for each of nh heads.  Head hh's partials
 // are slots (row0 + hh) * stride + first + i, i < cnt, of (src_o, src_ml); the result
 // goes to the output rows (normalised, rounded) when out is given, else to slot
@@ -139,7 +141,7 @@ __device__ void merge_partials(const float* src_o, const float* src_ml, int64_t 
 // NTL: K and V are loaded non-temporally (no table shares a block, so every byte is
 // read once per call); otherwise with the default policy, so that blocks several
 // tables share stay in L2 and the Infinity Cache for the other sequences.
-template <typename T, int D, int BS, bool NTL>
+template <typename T, int D, int BS, bool NTL, bool FUSE>
 __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_kernel(DecodeParams P) {
   typedef Chunk<T, D> C;
   constexpr int IDS = 32 / BS;  // physical blocks a 32-token chunk spans
@@ -151,6 +153,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   __shared__ float sm_l[NW][16];
   __shared__ int sm_bad[NW];
   __shared__ int sm_len[kScanMax];       // seq_lens of the launch's sequences
+  __shared__ int64_t sm_slot[FUSE ? kScanMax : 1];  // (fused write) slot_mapping of the sequences
   __shared__ int sm_full[kScanMax + 1];  // exclusive prefix count of full partitions
   __shared__ int sm_class[kScanMax];     // size class of each sequence's last partition
   __shared__ int sm_last[kScanMax];      // sequences in the order their last partitions run
@@ -170,6 +173,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   const int S = P.num_seqs, Hq = P.num_q_heads;
   int PT = P.part_tokens;  // set by the plan when it chooses the partition size
   const int HT2 = P.num_kv_heads * P.head_tiles;
+
 
   // ---------------------------------------------------------------- plan
   // Thread t looks at sequences 4t .. 4t+3.  With the default partition size the
@@ -192,6 +196,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       if (s < S) {
         const int L = P.seq_lens[s];
         sm_len[s] = L;
+        if constexpr (FUSE) sm_slot[s] = P.slot_mapping[s];
         if (L > 0 && L <= P.max_tokens) Ls[i] = L;
       }
       lsum += (float)Ls[i];
@@ -450,6 +455,26 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       const T* kbase = (const T*)P.k_cache + (int64_t)g * tile;
       const T* vbase = (const T*)P.v_cache + (int64_t)g * tile;
       const int32_t AS4* tbl = (const int32_t AS4*)(P.block_tables + (int64_t)s * P.max_blocks);
+      // (fused write) this item holds the sequence's last position, whose slot the launch
+      // writes: when slot_mapping[s] is that position's slot (checked where the chunk's
+      // block ids are at hand), the chunk holding it takes the token's key from k_new (a
+      // different load address for the lanes of that row) and its value from vnew, this
+      // wave's copy of the v_new row (VW 4-byte words a lane), patched into the value tile
+      constexpr int VW = D * (int)sizeof(T) > 256 ? 2 : 1;
+      const bool fused_last = FUSE && t_end == L;
+      bool red = false;
+      int64_t new_slot = -1;
+      uint32_t vnew[VW] = {};
+      const T* knew_row = nullptr;
+      if (fused_last) {
+        new_slot = sm_slot[s];
+        knew_row = (const T*)P.k_new + ((int64_t)s * P.num_kv_heads + g) * D;
+        const uint32_t* vr =
+            (const uint32_t*)((const T*)P.v_new + ((int64_t)s * P.num_kv_heads + g) * D);
+#pragma unroll
+        for (int w = 0; w < VW; ++w)
+          vnew[w] = (64 * w + lane) * 4 < D * (int)sizeof(T) ? vr[64 * w + lane] : 0u;
+      }
 
       float m_run = -INFINITY, l_run = 0.f;
       f32x4 acc[NT];
@@ -486,6 +511,15 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
         };
         const T* pa = kbase + (int64_t)pick(ra) * blk_stride + kofs_a;
         const T* pb = kbase + (int64_t)pick(rb) * blk_stride + kofs_b;
+        if (FUSE && fused_last && t0 + 32 >= L) {  // (uniform) the chunk of the written slot
+          int id_last = 0;  // the block id of the last position, one of this chunk's
+#pragma unroll
+          for (int i = 0; i < IDS; ++i)
+            if (j0 + i == last_blk) id_last = ids[i];
+          red = new_slot == (int64_t)id_last * BS + (L - 1) % BS;
+          if (red && t0 + ka == L - 1) pa = knew_row + quad * EPL;
+          if (red && t0 + ka + 4 == L - 1) pb = knew_row + quad * EPL;
+        }
 #pragma unroll
         for (int k = 0; k < C::KL; ++k) {
           c.ka[k] = ld16_as<NTL>(pa + k * 4 * EPL);
@@ -560,6 +594,26 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
 #pragma unroll
               for (int e = 0; e < 8; ++e)
                 c.v[nn][e >> 2][e & 3] = (tfirst + e < t_end) ? c.v[nn][e >> 2][e & 3] : 0u;
+            }
+          }
+        }
+        if (FUSE && red && t0 + 32 >= L) {  // (uniform) the written slot's value, from vnew
+          const int r = L - 1 - t0;   // its place in the chunk: segment r / 8, element r % 8
+          const int e = r & 7;
+#pragma unroll
+          for (int nn = 0; nn < NT; ++nn) {
+            const int d = 16 * nn + col;                  // this lane's dimension
+            const int wi = d * (int)sizeof(T) / 4;        // word of the v_new row holding it
+            const uint32_t word = (uint32_t)__builtin_amdgcn_ds_bpermute((wi & 63) << 2,
+                                                                         (int)vnew[(wi >> 6) % VW]);
+            if (quad == (r >> 3)) {
+              if constexpr (sizeof(T) == 2) {
+                const uint32_t h = (word >> (16 * (d & 1))) & 0xFFFFu;
+                const uint32_t x = c.v[nn][0][e >> 1];
+                c.v[nn][0][e >> 1] = (e & 1) ? ((x & 0x0000FFFFu) | (h << 16)) : ((x & 0xFFFF0000u) | h);
+              } else {
+                c.v[nn][e >> 2][e & 3] = word;
+              }
             }
           }
         }
@@ -724,47 +778,88 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
 
   if (pend) settle();
 
-  // the last workgroup out resets the queue for the next call
-  if (tid == 0) {
-    const int before = atomicAdd(P.queue + 1, 1);
-    if (before == (int)gridDim.x - 1) {
-      atomicExch(P.queue, 0);
-      atomicExch(P.queue + 1, 0);
+  // ---------------------------------------------------------------- fused cache write
+  // (pa_cache_write_decode) Each sequence's new token goes to its slot, a bit copy of its
+  // key row and value column ([RK] 分页注意力是如何工作的: the new token takes the next slot
+  // of its sequence's last block).  The stores are done by the workgroups that run out of
+  // items first: the k-th to finish stores rows kWriteRows * (k + i * grid), so the last
+  // ones to finish have none and the stores fill time the early finishers would sit idle.
+  // Nothing in this launch reads a slot written here: the chunk that holds a sequence's
+  // last position took that token's key and value from k_new / v_new (see `red`).
+  int finished_before = 0;  // (thread 0, and every thread when FUSE) workgroups finished before this one
+  if (tid == 0) finished_before = atomicAdd(P.queue + 1, 1);
+  if constexpr (FUSE) {
+    if (tid == 0) sm_flag[0] = finished_before;
+    __syncthreads();
+    finished_before = sm_flag[0];
+    constexpr int KP = D * (int)sizeof(T) / 16;  // 16-byte pieces of a key row
+    const int Hkv = P.num_kv_heads;
+    const int rows = S * Hkv;                    // (token, KV head) rows
+    for (int r0 = finished_before * kWriteRows; r0 < rows; r0 += (int)gridDim.x * kWriteRows) {
+      const int nr = min(kWriteRows, rows - r0);
+      for (int u = tid; u < nr * KP; u += NT_THREADS) {
+        const int64_t iu = r0 + u / KP;
+        const int piece = u % KP;
+        const int64_t slot = P.slot_mapping[iu / Hkv];
+        if (slot < 0 || slot >= P.num_slots) continue;
+        const int64_t g = iu % Hkv;
+        T* dst = (T*)P.k_cache + (((slot / BS) * Hkv + g) * BS + slot % BS) * D + piece * EPL;
+        *reinterpret_cast<u32x4*>(dst) = ld16((const T*)P.k_new + iu * D + piece * EPL);
+      }
+      for (int u = tid; u < nr * D; u += NT_THREADS) {
+        const int64_t iu = r0 + u / D;
+        const int d = u % D;
+        const int64_t slot = P.slot_mapping[iu / Hkv];
+        if (slot < 0 || slot >= P.num_slots) continue;
+        const int64_t g = iu % Hkv;
+        ((T*)P.v_cache)[(((slot / BS) * Hkv + g) * D + d) * BS + slot % BS] =
+            ((const T*)P.v_new)[iu * D + d];
+      }
     }
+  }
+
+  // the last workgroup out resets the queue for the next call
+  if (tid == 0 && finished_before == (int)gridDim.x - 1) {
+    atomicExch(P.queue, 0);
+    atomicExch(P.queue + 1, 0);
   }
 }
 
+// FUSE: the instance behind pa_cache_write_decode (new tokens stored in the same launch)
 template <typename T, int D, int BS>
-const void* kernel_of(bool stream_kv) {
-  return stream_kv ? (const void*)decode_kernel<T, D, BS, true>
-                   : (const void*)decode_kernel<T, D, BS, false>;
+const void* kernel_of(bool stream_kv, bool fuse) {
+  if (fuse)
+    return stream_kv ? (const void*)decode_kernel<T, D, BS, true, true>
+                     : (const void*)decode_kernel<T, D, BS, false, true>;
+  return stream_kv ? (const void*)decode_kernel<T, D, BS, true, false>
+                   : (const void*)decode_kernel<T, D, BS, false, false>;
 }
 
 template <typename T, int D>
-const void* kernel_bs(int bs, bool nt) {
+const void* kernel_bs(int bs, bool nt, bool fu) {
   switch (bs) {
-    case 4: return kernel_of<T, D, 4>(nt);
-    case 8: return kernel_of<T, D, 8>(nt);
-    case 16: return kernel_of<T, D, 16>(nt);
-    case 32: return kernel_of<T, D, 32>(nt);
+    case 4: return kernel_of<T, D, 4>(nt, fu);
+    case 8: return kernel_of<T, D, 8>(nt, fu);
+    case 16: return kernel_of<T, D, 16>(nt, fu);
+    case 32: return kernel_of<T, D, 32>(nt, fu);
   }
   return nullptr;
 }
 
 template <typename T>
-const void* kernel_d(int d, int bs, bool nt) {
+const void* kernel_d(int d, int bs, bool nt, bool fu) {
   switch (d) {
-    case 64: return kernel_bs<T, 64>(bs, nt);
-    case 128: return kernel_bs<T, 128>(bs, nt);
+    case 64: return kernel_bs<T, 64>(bs, nt, fu);
+    case 128: return kernel_bs<T, 128>(bs, nt, fu);
   }
   return nullptr;
 }
 
-const void* decode_kernel_for(int dtype, int head_dim, int block_size, bool nt) {
+const void* decode_kernel_for(int dtype, int head_dim, int block_size, bool nt, bool fu) {
   switch (dtype) {
-    case 0: return kernel_d<float>(head_dim, block_size, nt);
-    case 1: return kernel_d<_Float16>(head_dim, block_size, nt);
-    case 2: return kernel_d<__bf16>(head_dim, block_size, nt);
+    case 0: return kernel_d<float>(head_dim, block_size, nt, fu);
+    case 1: return kernel_d<_Float16>(head_dim, block_size, nt, fu);
+    case 2: return kernel_d<__bf16>(head_dim, block_size, nt, fu);
   }
   return nullptr;
 }
@@ -773,7 +868,8 @@ const void* decode_kernel_for(int dtype, int head_dim, int block_size, bool nt) 
 
 hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodeParams& p,
                          int grid, hipStream_t stream) {
-  const void* k = decode_kernel_for(dtype, head_dim, block_size, p.stream_kv != 0);
+  const void* k = decode_kernel_for(dtype, head_dim, block_size, p.stream_kv != 0,
+                                    p.slot_mapping != nullptr);
   if (!k || grid <= 0) return hipErrorInvalidValue;
   DecodeParams arg = p;
   void* args[] = {&arg};
@@ -781,8 +877,9 @@ hipError_t launch_decode(int dtype, int head_dim, int block_size, const DecodePa
 }
 
 hipError_t decode_blocks_per_cu(int dtype, int head_dim, int block_size, int* blocks) {
-  // the two cache-policy variants use the same resources
-  const void* k = decode_kernel_for(dtype, head_dim, block_size, true);
+  // the cache-policy and fused-write variants are all compiled for the same workgroups
+  // per compute unit (their launch bounds)
+  const void* k = decode_kernel_for(dtype, head_dim, block_size, true, false);
   if (!k) return hipErrorInvalidValue;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k, NT_THREADS, 0);
 }

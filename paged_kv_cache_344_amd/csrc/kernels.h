@@ -49,6 +49,11 @@ struct DecodeParams {
   int32_t pmax;                 // ceil(max_tokens / part_tokens)
   int32_t nodes;                // ceil(pmax / kMergeFan)
   float scale_log2;             // scale * log2(e): logits are kept in base-2 units
+  // fused cache write (pa_cache_write_decode), else slot_mapping is null
+  const void* k_new;            // [S][Hkv][D]: sequence s's new token, at position seq_lens[s]-1
+  const void* v_new;            // [S][Hkv][D]
+  const int64_t* slot_mapping;  // [S]: the new tokens' slots (< 0 or >= num_slots: none)
+  int64_t num_slots;            // N * bs
 };
 
 struct CacheWriteParams {

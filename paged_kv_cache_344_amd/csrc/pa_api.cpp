@@ -264,10 +264,18 @@ pa_status check_decode_args(const void* q, const void* k_cache, const void* v_ca
 
 // The decode launches of a checked call, with ws (of at least pl.ws_bytes bytes) as the
 // workspace.
+// Fused cache write of pa_cache_write_decode: one new token per sequence (row s of
+// k and v), to slot slot_mapping[s].
+struct NewTokens {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const int64_t* slot_mapping = nullptr;
+};
+
 pa_status decode_launches(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, const int32_t* seq_lens, int32_t block_size,
                           int32_t num_kv_heads, float scale, void* out, const pa_decode_ext* ext,
-                          const Plan& pl, char* ws) {
+                          const Plan& pl, char* ws, const NewTokens& nt = NewTokens()) {
   int grid = 0;
   pa_status st = decode_grid(ext->dtype, ext->head_dim, block_size, &grid);
   if (st != PA_OK) return st;
@@ -288,6 +296,7 @@ pa_status decode_launches(const void* q, const void* k_cache, const void* v_cach
   p.nodes = pl.nodes;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);  // log2(e)
   p.queue = reinterpret_cast<int32_t*>(ws);
+  p.num_slots = ext->num_blocks * block_size;
 
   const size_t esz = ext->dtype == PA_F32 ? 4 : 2;
   hipStream_t stream = static_cast<hipStream_t>(ext->stream);
@@ -302,6 +311,10 @@ pa_status decode_launches(const void* q, const void* k_cache, const void* v_cach
     p.block_tables = block_tables + (size_t)s0 * ext->max_blocks_per_seq;
     p.seq_lens = seq_lens + s0;
     p.num_seqs = n;
+    const size_t new_rows = (size_t)s0 * num_kv_heads * D * esz;
+    p.k_new = nt.slot_mapping ? static_cast<const char*>(nt.k) + new_rows : nullptr;
+    p.v_new = nt.slot_mapping ? static_cast<const char*>(nt.v) + new_rows : nullptr;
+    p.slot_mapping = nt.slot_mapping ? nt.slot_mapping + s0 : nullptr;
     p.node_count = reinterpret_cast<int32_t*>(ws + pl.off_node_count) + (size_t)s0 * ht2 * pl.nodes;
     p.root_count = reinterpret_cast<int32_t*>(ws + pl.off_root_count) + (size_t)s0 * ht2;
     p.part_o = reinterpret_cast<float*>(ws + pl.off_part_o) + rows0 * pl.pmax * D;
@@ -341,6 +354,34 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (!aligned(ext->workspace, 16)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   return decode_launches(q, k_cache, v_cache, block_tables, seq_lens, block_size, num_kv_heads,
                          scale, out, ext, pl, static_cast<char*>(ext->workspace));
+}
+
+pa_status pa_cache_write_decode(const void* k, const void* v, const int64_t* slot_mapping,
+                                const void* q, void* k_cache, void* v_cache,
+                                const int32_t* block_tables, const int32_t* seq_lens,
+                                int32_t block_size, int32_t num_kv_heads, float scale, void* out,
+                                const pa_decode_ext* ext) {
+  g_error.clear();
+  Plan pl;
+  pa_status st = plan_decode(ext, block_size, num_kv_heads, &pl);
+  if (st != PA_OK) return st;
+  if (ext->num_seqs == 0) return PA_OK;
+  st = check_decode_args(q, k_cache, v_cache, block_tables, seq_lens, scale, out);
+  if (st != PA_OK) return st;
+  if (!k || !v || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "k, v or slot_mapping is NULL");
+  if (!aligned(k, 16) || !aligned(v, 16)) return fail(PA_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  if (!aligned(slot_mapping, 8)) return fail(PA_ERR_INVALID_ARG, "slot_mapping must be 8-byte aligned");
+  if (ext->num_blocks > INT64_MAX / block_size) return fail(PA_ERR_INVALID_ARG, "num_blocks too large");
+  if (!ext->workspace || ext->workspace_bytes < pl.ws_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.ws_bytes,
+                ext->workspace ? ext->workspace_bytes : (size_t)0);
+  if (!aligned(ext->workspace, 16)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  NewTokens nt;
+  nt.k = k;
+  nt.v = v;
+  nt.slot_mapping = slot_mapping;
+  return decode_launches(q, k_cache, v_cache, block_tables, seq_lens, block_size, num_kv_heads,
+                         scale, out, ext, pl, static_cast<char*>(ext->workspace), nt);
 }
 
 pa_status pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,

@@ -154,6 +154,44 @@ def test_decode_rejects_null_and_misaligned(lib):
     assert _decode(lib, _ext(num_seqs=0), ptr=0) == B.PA_OK
 
 
+def _wd(lib, ext, k=FAKE, v=FAKE, slots=FAKE, ptr=FAKE, bs=16, hkv=8):
+    return lib.pa_cache_write_decode(k, v, slots, ptr, ptr, ptr, ptr, ptr, bs, hkv,
+                                     ctypes.c_float(0.088), ptr,
+                                     ctypes.byref(ext) if ext is not None else None)
+
+
+def test_cache_write_decode_rejects(lib):
+    """The fused step checks what pa_decode checks, plus its k, v and slot_mapping, all
+    before anything is launched."""
+    ws = dict(workspace=FAKE, workspace_bytes=1 << 40)
+    assert _wd(lib, None) == B.PA_ERR_INVALID_ARG
+    assert _wd(lib, _ext(head_dim=100, **ws)) == B.PA_ERR_UNSUPPORTED
+    assert _wd(lib, _ext(**ws), k=0) == B.PA_ERR_INVALID_ARG
+    assert _wd(lib, _ext(**ws), v=0) == B.PA_ERR_INVALID_ARG
+    assert _wd(lib, _ext(**ws), slots=0) == B.PA_ERR_INVALID_ARG
+    assert _wd(lib, _ext(**ws), k=FAKE + 8) == B.PA_ERR_INVALID_ARG
+    assert _wd(lib, _ext(**ws), slots=FAKE + 4) == B.PA_ERR_INVALID_ARG
+    assert _wd(lib, _ext()) == B.PA_ERR_WORKSPACE          # no workspace
+    assert lib.pa_last_error()
+    assert _wd(lib, _ext(num_seqs=0), k=0, v=0, slots=0, ptr=0) == B.PA_OK  # nothing to do
+
+
+def test_decode_noalloc_rejects_before_touching_the_gpu(lib):
+    """pa_decode_noalloc refuses shapes whose workspace would exceed its static scratch
+    (64 MiB) and bad arguments, without any HIP call (this machine has no GPU)."""
+    def na(ext, ptr=FAKE):
+        return lib.pa_decode_noalloc(ptr, ptr, ptr, ptr, ptr, 16, 8, ctypes.c_float(0.088), ptr,
+                                     ctypes.byref(ext) if ext is not None else None)
+    big = _ext(partition_size=32)            # 8 seqs x 32 heads x 4096 partitions of partials
+    st, need = _ws(lib, big)
+    assert st == B.PA_OK and need > (64 << 20)
+    assert na(big) == B.PA_ERR_WORKSPACE
+    assert na(None) == B.PA_ERR_INVALID_ARG
+    assert na(_ext(head_dim=100)) == B.PA_ERR_UNSUPPORTED
+    assert na(_ext(partition_size=-1), ptr=0) == B.PA_ERR_INVALID_ARG
+    assert na(_ext(num_seqs=0), ptr=0) == B.PA_OK
+
+
 def _cw(lib, ptr=FAKE, slot_ptr=None, **kw):
     base = dict(num_tokens=128, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=100,
                 dtype=B.PA_BF16, stream=None)
