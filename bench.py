@@ -378,10 +378,27 @@ def parity(out, ref, dtype):
     return res
 
 
+def _product_code(text):
+    """The source as the product library compiles it: without the diagnostic
+    PA_DECODE_TRACE sections (not nested, each closed by the first #endif) and without
+    whole-line comments, so that editing either leaves the digest alone."""
+    out, skip = [], False
+    for line in text.splitlines():
+        s = line.strip()
+        if s.startswith("#ifdef PA_DECODE_TRACE"):
+            skip = True
+        elif skip:
+            skip = not s.startswith("#endif")
+        elif s and not s.startswith("//"):
+            out.append(line)
+    return "\n".join(out)
+
+
 def source_digest():
     h = hashlib.sha256()
     for f in ("decode.hip", "decode_common.h", "cache_write.hip", "kernels.h"):
-        h.update(open(os.path.join(ROOT, "paged_kv_cache_344_amd", "csrc", f), "rb").read())
+        path = os.path.join(ROOT, "paged_kv_cache_344_amd", "csrc", f)
+        h.update(_product_code(open(path).read()).encode())
     return h.hexdigest()[:16]
 
 

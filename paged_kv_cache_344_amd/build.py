@@ -14,6 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libpa.so")
+# diagnostic build: the same library with the decode kernel recording per-item timestamps
+TRACE_LIB_PATH = os.path.join(PKG, "libpa_trace.so")
 SOURCES = ["decode.hip", "cache_write.hip", "copy_blocks.hip", "multi_token.hip", "noalloc.hip",
            "pa_api.cpp", "block_manager.cpp"]
 
@@ -34,20 +36,25 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def compile_command(src: str, obj: str) -> list:
-    return [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+def compile_command(src: str, obj: str, extra=()) -> list:
+    return [hipcc(), *FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src),
+            "-o", obj]
 
 
 def link_command(objs: list, out: str) -> list:
     return [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out]
 
 
-def build(verbose: bool = False, check: bool = True) -> str:
+def build(verbose: bool = False, check: bool = True, trace: bool = False) -> str:
+    """Build libpa.so (or, with trace, the diagnostic libpa_trace.so whose decode kernel
+    records per-item timestamps; see trace_decode.py) and return its path."""
+    out_path = TRACE_LIB_PATH if trace else LIB_PATH
+    extra = ["-DPA_DECODE_TRACE"] if trace else []
     with tempfile.TemporaryDirectory(prefix="libpa_build_") as tmp:
         objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
 
         def one(i):
-            cmd = compile_command(SOURCES[i], objs[i])
+            cmd = compile_command(SOURCES[i], objs[i], extra)
             if verbose:
                 print(" ".join(cmd), flush=True)
             subprocess.run(cmd, check=True)
@@ -65,10 +72,10 @@ def build(verbose: bool = False, check: bool = True) -> str:
             rep = codecheck.check(tmp_lib)
             if verbose:
                 print(f"machine-code checks passed: {rep}", flush=True)
-        shutil.copyfile(tmp_lib, LIB_PATH + ".tmp")
-        os.chmod(LIB_PATH + ".tmp", 0o755)
-        os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+        shutil.copyfile(tmp_lib, out_path + ".tmp")
+        os.chmod(out_path + ".tmp", 0o755)
+        os.replace(out_path + ".tmp", out_path)
+    return out_path
 
 
 if __name__ == "__main__":

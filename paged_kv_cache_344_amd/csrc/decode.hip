@@ -81,6 +81,21 @@ using namespace dec;
 
 constexpr int kWriteRows = 16;  // (token, KV head) rows a workgroup stores per claim (fused write)
 
+// Diagnostic build only (PA_DECODE_TRACE, a separate library, never the product one):
+// every workgroup records s_memrealtime stamps (100 MHz) of its plan and of its first
+// kTraceItems items in kTraceWords words of pa_trace_buf: [0] entry, [1] plan done, [2 + 4k ..
+// 5 + 4k] item k's start, end of its chunk loop, end of its epilogue and (queue position,
+// one-chunk group flag << 32, past-the-regular-items flag << 33, tokens << 34), [248]
+// lengths read,
+// [250] partition length, [254] items taken, [255] exit.  Read back with
+// pa_decode_trace_read; paged_kv_cache_344_amd/trace_decode.py prints the timeline.
+#ifdef PA_DECODE_TRACE
+constexpr int kTraceWords = 256;
+constexpr int kTraceItems = 60;
+__device__ unsigned long long pa_trace_buf[2048 * kTraceWords];
+#define PA_TRACE_STAMP() __builtin_amdgcn_s_memrealtime()
+#endif
+
 // Log-sum-exp combination of cnt partials for each of nh heads.  Head hh's partials
 // are slots (row0 + hh) * stride + first + i, i < cnt, of (src_o, src_ml); the result
 // goes to the output rows (normalised, rounded) when out is given, else to slot
@@ -164,6 +179,11 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   __shared__ float sm_wsumf[NW];
   __shared__ int sm_next[2];  // by item parity: an item may pass no barrier before the next write
   __shared__ int sm_flag[2];
+#ifdef PA_DECODE_TRACE
+  const unsigned long long tr_t0 = PA_TRACE_STAMP();
+  unsigned long long* tr = pa_trace_buf + (blockIdx.x & 2047) * kTraceWords;
+  int tr_n = 0;
+#endif
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -213,6 +233,9 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       const float want = fminf(kPartShare * share, (float)P.max_tokens);
       PT = max(PT, ((int)want + 128) / 256 * 256);  // nearest multiple of 256
     }
+#ifdef PA_DECODE_TRACE
+    if (threadIdx.x == 0) tr[248] = PA_TRACE_STAMP();
+#endif
     int nfull[4], cls[4], sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -319,6 +342,13 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
     planned = true;
   }
 
+#ifdef PA_DECODE_TRACE
+  if (threadIdx.x == 0) {
+    tr[0] = tr_t0;
+    tr[1] = PA_TRACE_STAMP();
+    tr[250] = PT;
+  }
+#endif
   // table entries are int32, so a pool larger than INT32_MAX blocks accepts them all
   const uint32_t nblk32 = (uint32_t)min(P.num_blocks, (int64_t)0x7fffffff);
   const int64_t tile = (int64_t)BS * D;  // elements of one (block, KV head) tile
@@ -385,6 +415,11 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
     // the short ones last) instead of being held by a workgroup for a whole item while
     // others go idle, early enough that the atomic's round trip overlaps the last chunk
     // and the epilogue.
+#ifdef PA_DECODE_TRACE
+    const unsigned long long tr_is = PA_TRACE_STAMP();
+    unsigned long long tr_il = 0;
+    int tr_tok = 0;  // the item's tokens
+#endif
     int next = 0;
     bool took = false;
     auto take_next = [&]() {
@@ -441,6 +476,9 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       const int t_begin = p * PT;
       const int t_end = min(L, t_begin + PT);
       const int nchunks = (t_end - t_begin + 31) >> 5;
+#ifdef PA_DECODE_TRACE
+      tr_tok = t_end - t_begin;
+#endif
       const int last_blk = (L - 1) / BS;  // last table entry the sequence uses
 
       // query fragment: lane (c, i) holds the same slice of q[head c] that it holds
@@ -682,6 +720,9 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       planned = true;
       if (!took) take_next();  // (wave 0 always has a chunk; kept for safety)
 
+#ifdef PA_DECODE_TRACE
+      tr_il = PA_TRACE_STAMP();
+#endif
       if (tiny) {
         // a one-chunk sequence of this wave alone: normalise and store, no merge
         if (active) {
@@ -765,6 +806,18 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       }  // not a one-chunk group
     }
 
+#ifdef PA_DECODE_TRACE
+    if (threadIdx.x == 0 && tr_n < kTraceItems) {
+      tr[2 + 4 * tr_n] = tr_is;
+      tr[3 + 4 * tr_n] = tr_il;
+      tr[4 + 4 * tr_n] = PA_TRACE_STAMP();
+      tr[5 + 4 * tr_n] = (unsigned long long)(unsigned)item |
+                         ((unsigned long long)(tiny ? 1 : 0) << 32) |
+                         ((unsigned long long)(planned && item >= A ? 1 : 0) << 33) |
+                         ((unsigned long long)tr_tok << 34);
+    }
+    ++tr_n;
+#endif
     // Two slots: thread 0 may write the next item's slot before a slow wave has read
     // this one only if the item in between passes no barrier (the fill path).
     if (!planned) {  // (not reached: the first item of such a workgroup is a full one)
@@ -777,6 +830,13 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   }
 
   if (pend) settle();
+
+#ifdef PA_DECODE_TRACE
+  if (threadIdx.x == 0) {
+    tr[254] = (unsigned long long)tr_n;
+    tr[255] = PA_TRACE_STAMP();
+  }
+#endif
 
   // ---------------------------------------------------------------- fused cache write
   // (pa_cache_write_decode) Each sequence's new token goes to its slot, a bit copy of its
@@ -885,3 +945,12 @@ hipError_t decode_blocks_per_cu(int dtype, int head_dim, int block_size, int* bl
 }
 
 }  // namespace pa
+
+#ifdef PA_DECODE_TRACE
+// (diagnostic build) copy the trace buffer of the last decode launch to host memory
+extern "C" __attribute__((visibility("default"))) int pa_decode_trace_read(void* host, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(pa::pa_trace_buf),
+                                  bytes < sizeof(pa::pa_trace_buf) ? bytes : sizeof(pa::pa_trace_buf),
+                                  0, hipMemcpyDeviceToHost);
+}
+#endif
