@@ -331,13 +331,19 @@ def copy_ceiling(nbytes=2 << 30, reps=5):
 
 
 def cpu_model():
-    """The host CPU's model name as lscpu reports it (/proc/cpuinfo if lscpu is missing)."""
+    """The host CPU's model name as lscpu reports it, with its family / model / stepping
+    numbers (a virtual machine may name only the product line), or /proc/cpuinfo's."""
     import subprocess
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        f = {}
         for line in out.splitlines():
-            if line.strip().startswith("Model name:"):
-                return line.split(":", 1)[1].strip()
+            k, _, v = line.partition(":")
+            f.setdefault(k.strip(), v.strip())
+        if f.get("Model name"):
+            ids = ", ".join(f"{k.lower()} {f[k]}" for k in ("CPU family", "Model", "Stepping")
+                            if f.get(k))
+            return f"{f['Model name']} ({ids})" if ids else f["Model name"]
     except (OSError, subprocess.SubprocessError):
         pass
     try:

@@ -37,6 +37,8 @@ def main(argv=None):
     ap.add_argument("batch", nargs="?", default="gqa_bf16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--reps", type=int, default=12)
+    ap.add_argument("--dump", default=None,
+                    help="also save the raw per-workgroup words (.npy) for offline reading")
     args = ap.parse_args(argv)
     if not os.path.exists(TRACE_LIB_PATH):
         raise SystemExit(f"{TRACE_LIB_PATH} is not built: build.build(trace=True) first")
@@ -76,6 +78,8 @@ def main(argv=None):
         ev_us = e0.elapsed_time(e1) * 1e3
         if L.pa_decode_trace_read(buf.ctypes.data, buf.nbytes) != 0:
             raise SystemExit("pa_decode_trace_read failed")
+    if args.dump:
+        np.save(args.dump, buf.reshape(MAX_WG, SLOTS))
     summarise(b, buf.reshape(MAX_WG, SLOTS).astype(np.int64), ev_us)
 
 
