@@ -8,7 +8,8 @@ build (the AMD assembly of our own code objects, disassembled with ROCm's llvm-o
    inline assembly that sets M0 (the LDS destination) right before each load; the
    compiler cannot keep a value of its own live in M0 across such a statement, so the
    check requires that no compiler-generated instruction reads or writes M0 at all:
-   every instruction naming M0 must be `s_mov_b32 m0, sN` directly followed by
+   every instruction naming M0 must be `s_mov_b32 m0, <SGPR>` (sN, or the VCC halves
+   the allocator may also hand an "s" operand) directly followed by
    `s_nop 0` and a `global_load_lds_*`, every `global_load_lds_*` must come right after
    such a pair, and no instruction that uses M0 implicitly (indexed register moves,
    messages, GWS, LDS-append, other LDS-DMA forms) may appear.
@@ -26,6 +27,7 @@ MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 
 PACKED_FP32 = re.compile(r"\bv_pk_(add|mul|fma)_f32\b")
 NAMES_M0 = re.compile(r"\bm0\b")
+SETUP_M0 = re.compile(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)")
 IMPLICIT_M0 = re.compile(r"\b(s_movrel\w*|v_movrel\w*|s_sendmsg\w*|ds_gws_\w+|ds_append|ds_consume|"
                          r"ds_read_addtid\w*|ds_write_addtid\w*|buffer_load_\w+\s.*\blds\b|"
                          r"buffer_store_lds\w*|s_set_gpr_idx_\w+)")
@@ -88,12 +90,12 @@ def problems(texts: list) -> list:
             if IMPLICIT_M0.search(s):
                 bad.append(f"instruction that uses M0 implicitly in {fn}: {s}")
             if s.startswith("global_load_lds"):
-                ok = (i >= 2 and re.fullmatch(r"s_mov_b32 m0, s\d+", ins[i - 2][1])
+                ok = (i >= 2 and SETUP_M0.fullmatch(ins[i - 2][1])
                       and ins[i - 1][1] == "s_nop 0")
                 if not ok:
                     bad.append(f"LDS-DMA load without its own M0 set-up in {fn}: {s}")
             elif NAMES_M0.search(s):
-                ok = (re.fullmatch(r"s_mov_b32 m0, s\d+", s) and i + 2 < len(ins)
+                ok = (SETUP_M0.fullmatch(s) and i + 2 < len(ins)
                       and ins[i + 1][1] == "s_nop 0" and ins[i + 2][1].startswith("global_load_lds"))
                 if not ok:
                     bad.append(f"M0 used outside an LDS-DMA load sequence in {fn}: {s}")

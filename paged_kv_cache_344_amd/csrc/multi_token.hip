@@ -51,6 +51,7 @@
 // dispatched to the eight XCDs in turn; the numbering deals whole (sequence, KV head) groups to
 // the XCDs round-robin, so that the row tiles of a group share their XCD's L2 copy of
 // the K/V they all read, and every XCD gets a share of every sequence.
+#include <float.h>
 #include <math.h>
 
 #include <type_traits>
@@ -248,14 +249,20 @@ __device__ __forceinline__ void wait_loads_and_sync() {
 }
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// NTL: K/V staging loads are non-temporal.  Used when each (sequence, KV head) has one
-// row tile, so every K/V byte is read by one workgroup (draft-token verification);
-// several row tiles share each chunk through L2 (prompt chunks) and keep the default.
-template <typename T, int D, int BS, bool NTL>
-__global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_kernel(MultiTokenParams P) {
+// ONE_TILE: every (sequence, KV head) has one row tile (at most 128 rows, e.g. draft
+// tokens).  Then every K/V byte is read by one workgroup, so the staging loads are
+// non-temporal, and a wave skips a tile that holds no row of the problem.  Otherwise
+// several row tiles share each chunk through L2 (prompt chunks): the staging loads keep
+// the default policy, and a wave with any row computes both of its tiles (a tile with
+// no row repeats a live row and is never stored).  With no per-tile branch the 16-bit
+// chunk body needs few enough registers (168) for three workgroups a CU, whose waves
+// overlap one another's MFMA and VALU work on each SIMD.
+template <typename T, int D, int BS, bool ONE_TILE>
+__global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? (ONE_TILE ? 2 : 3) : 1) void multi_token_kernel(MultiTokenParams P) {
   typedef Shape<T, D, BS> SH;
   constexpr int KL = SH::KL, NT = SH::NT, EPL = SH::EPL, KSEG = SH::KSEG, TPS = SH::TPS;
-  constexpr int NBUF = SH::NBUF;
+  // three workgroups a CU for the all-tiles 16-bit instance: three chunk buffers
+  constexpr int NBUF = (!ONE_TILE && sizeof(T) == 2 && SH::NBUF == 4) ? 3 : SH::NBUF;
 
   __shared__ __attribute__((aligned(16))) T sk[NBUF][SH::CHUNK];
   __shared__ __attribute__((aligned(16))) T sv[NBUF][SH::CHUNK];
@@ -319,7 +326,9 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
   // ---- this lane's rows: query fragments and causal limits.  A negative scale is
   // applied as |scale| to queries with their sign bits flipped (exact), so that the
   // largest logit is the largest raw dot product.
-  const float sc = fabsf(P.scale_log2);
+  // (a zero scale is taken as FLT_MIN: the same weights, all exactly 1, but a masked
+  // logit of -inf then stays -inf after scaling instead of becoming NaN)
+  const float sc = fabsf(P.scale_log2) == 0.f ? FLT_MIN : fabsf(P.scale_log2);
   const uint32_t qsign = P.scale_log2 < 0.f ? (sizeof(T) == 2 ? 0x80008000u : 0x80000000u) : 0u;
   // Row tile t of wave w holds rows 16 (w + 4t) .. 16 (w + 4t) + 15 of the workgroup's
   // 128, so that a workgroup with few rows (a few new tokens) spreads them over its
@@ -405,7 +414,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
         const int id1 = checked(kid[i][1]);
         id = lane >= 32 ? id1 : id;
       }
-      load_to_lds<16, NTL>(kbase + (int64_t)id * blk_stride + koff[i],
+      load_to_lds<16, ONE_TILE>(kbase + (int64_t)id * blk_stride + koff[i],
                       &sk[buf][64 * (wave + WAVES * i) * EPL]);
     }
 #pragma unroll
@@ -415,7 +424,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
         const int id1 = checked(vid[i][1]);
         id = (lane & 2) ? id1 : id;
       }
-      load_to_lds<SH::VB, NTL>(vbase + (int64_t)id * blk_stride + voff[i],
+      load_to_lds<SH::VB, ONE_TILE>(vbase + (int64_t)id * blk_stride + voff[i],
                           &sv[buf][64 * (wave + WAVES * i) * SH::VB / SH::E]);
     }
   };
@@ -441,6 +450,8 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
     f32x4 sa[NTILE], sb[NTILE];
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) sa[t] = sb[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // every tile of a live wave (see ONE_TILE); fp32 keeps the per-tile order below
+    constexpr bool ALL = !ONE_TILE && sizeof(T) == 2;
     // key rows col (tile a) and 16 + col (tile b) share their swizzle
     const T* ka = &sk[buf][col * KSEG * EPL];
     const T* kb = ka + 16 * KSEG * EPL;
@@ -451,7 +462,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
       const u32x4 b = *reinterpret_cast<const u32x4*>(kb + seg * EPL);
 #pragma unroll
       for (int t = 0; t < NTILE; ++t) {
-        if (t >= nlive) break;
+        if (!ALL && t >= nlive) break;
         if constexpr (sizeof(T) == 2) {
           typedef typename V8<T>::type VT;
           sa[t] = mma16(__builtin_bit_cast(VT, a), __builtin_bit_cast(VT, qf[t][k]), sa[t]);
@@ -471,6 +482,71 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
     const int tfirst = t0 + 8 * quad;
     // dimension 16nn + col, tokens 8quad .. 8quad + 7: value segment quad (two for fp32)
     const T* vrow = &sv[buf][(8 / TPS) * quad * D * TPS + col * TPS];
+    if constexpr (ALL) {
+      // Both tiles; masking first, on the logits (a masked logit is -inf, so its
+      // weight is exp2(-inf) = 0 with no second select); then tile 0's softmax and
+      // rescale, tile 1's softmax, tile 0's weighted sum, tile 1's rescale and weighted
+      // sum.  Per tile the operations and their order are those of the loop below, so
+      // the results are the same bits.
+      typedef typename V8<T>::type VT;
+      static_assert(NTILE == 2, "two row tiles a wave");
+      if (masked) {
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sa[t][e] = (tfirst + e <= lim[t]) ? sa[t][e] : -INFINITY;
+            sb[t][e] = (tfirst + 4 + e <= lim[t]) ? sb[t][e] : -INFINITY;
+          }
+      }
+      auto softmax = [&](int t, u32x4& hi, u32x4& lo) {
+        float z[8];  // raw dot products; the scale is applied inside the exponent
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          z[e] = sa[t][e];
+          z[4 + e] = sb[t][e];
+        }
+        const float cm = max_over_quads(max8(z));
+        const float m_new = fmaxf(m_run[t], cm * sc);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2_fast(m_run[t] - m_use);
+        float pr[8], psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(__builtin_fmaf(z[e], sc, -m_use));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) psum += pr[e];
+        l_run[t] = l_run[t] * alpha + psum;
+        m_run[t] = m_new;
+        split_weights<T>(pr, hi, lo);
+        return alpha;
+      };
+      auto rescale = [&](int t, float alpha) {
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+          for (int nn = 0; nn < NT; ++nn) acc[t][nn] *= alpha;
+        }
+      };
+      auto weighted_sum = [&](int t, const u32x4& hi, const u32x4& lo) {
+#pragma unroll
+        for (int nn = 0; nn < NT; ++nn) {
+          const VT vv = *reinterpret_cast<const VT*>(vrow + 16 * nn * TPS);
+          acc[t][nn] = mma16(vv, __builtin_bit_cast(VT, hi), acc[t][nn]);
+          if constexpr (std::is_same<T, __bf16>::value)
+            acc[t][nn] = mma16(vv, __builtin_bit_cast(VT, lo), acc[t][nn]);
+        }
+      };
+      u32x4 h0, l0, h1, l1;
+      rescale(0, softmax(0, h0, l0));
+      const float a1 = softmax(1, h1, l1);
+      weighted_sum(0, h0, l0);
+      rescale(1, a1);
+      // tile 1 reads the value operands again rather than keeping tile 0's live
+      uint32_t vaddr = (uint32_t)(uintptr_t)(lds_void*)vrow;
+      asm volatile("" : "+v"(vaddr));
+      vrow = (const T*)(lds_void*)(uintptr_t)vaddr;
+      weighted_sum(1, h1, l1);
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
       if (t >= nlive) break;
@@ -551,16 +627,19 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
 #pragma unroll
   for (int j = 0; j < NBUF - 1; ++j) {
     if (c_lo + j < nch) {
-      issue((c_lo + j) & (NBUF - 1));
+      issue((c_lo + j) % NBUF);
       if (c_lo + j + 1 < nch) load_ids(c_lo + j + 1);
     }
   }
   for (int c = c_lo; c < nch; ++c) {
-    const int buf = c & (NBUF - 1);
+    const int buf = c % NBUF;
     const int ahead = min(NBUF - 2, nch - 1 - c);  // chunks issued after this one
     if constexpr (NBUF == 4) {
       if (ahead >= 2) wait_loads_and_sync<2 * SH::LOADS>();
       else if (ahead == 1) wait_loads_and_sync<SH::LOADS>();
+      else wait_loads_and_sync<0>();
+    } else if constexpr (NBUF == 3) {
+      if (ahead >= 1) wait_loads_and_sync<SH::LOADS>();
       else wait_loads_and_sync<0>();
     } else {
       wait_loads_and_sync<0>();
@@ -574,7 +653,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? 2 : 1) void multi_token_k
       lds_sync();
     }
     if (c + NBUF - 1 < nch) {
-      issue((c + NBUF - 1) & (NBUF - 1));  // the buffer computed last iteration
+      issue((c + NBUF - 1) % NBUF);  // the buffer computed last iteration
       if (c + NBUF < nch) load_ids(c + NBUF);
     }
     compute(c, buf);

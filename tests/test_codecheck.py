@@ -15,8 +15,9 @@ def _probs(body: str):
     return codecheck.problems([HEAD + body])
 
 
-def test_clean_lds_dma_sequence_passes():
-    body = ("\ts_mov_b32 m0, s18 // 0\n\ts_nop 0 // 4\n"
+@pytest.mark.parametrize("sreg", ["s18", "vcc_hi", "vcc_lo"])
+def test_clean_lds_dma_sequence_passes(sreg):
+    body = (f"\ts_mov_b32 m0, {sreg} // 0\n\ts_nop 0 // 4\n"
             "\tglobal_load_lds_dwordx4 v[34:35], off nt // 8\n"
             "\tv_fma_f32 v0, v1, v2, v3 // c\n")
     assert _probs(body) == []
@@ -37,6 +38,8 @@ def test_packed_fp32_is_rejected(ins):
     ("\tv_movrels_b32 v1, v2 // 0\n", "implicitly"),
     ("\ts_sendmsg sendmsg(MSG_INTERRUPT) // 0\n", "implicitly"),
     ("\ts_mov_b32 s5, m0 // 0\n", "outside an LDS-DMA"),
+    ("\ts_mov_b32 m0, v3 // 0\n\ts_nop 0 // 4\n\tglobal_load_lds_dword v[1:2], off // 8\n",
+     "without its own M0"),
 ])
 def test_m0_misuse_is_rejected(body, what):
     p = _probs(body)
