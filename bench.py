@@ -172,7 +172,8 @@ class Copy:
             self.decode = pa.PreparedMultiToken(
                 self.q, self.kc, self.vc, self.bt, self.sl, self.qs, b.block_size,
                 b.num_kv_heads, b.scale, self.out,
-                max_query_len=int((b.query_start[1:] - b.query_start[:-1]).max()))
+                max_query_len=int((b.query_start[1:] - b.query_start[:-1]).max()),
+                max_seq_len=int(b.seq_lens.max()))  # a serving step knows its longest sequence
             return
         self.decode = pa.PreparedDecode(self.q, self.kc, self.vc, self.bt, self.sl, b.block_size,
                                         b.num_kv_heads, b.scale, self.out,

@@ -275,6 +275,10 @@ typedef struct pa_multi_token_ext {
                               /* unused (may be NULL) when the call does not split     */
   size_t workspace_bytes;     /* its size; see pa_multi_token_workspace_bytes          */
   void* stream;               /* hipStream_t                                           */
+  int32_t max_seq_len;        /* 0, or a bound L_max >= every seq_lens[s], at most     */
+                              /* max_blocks_per_seq * bs: the context split and its    */
+                              /* workspace are sized from it instead of the table's    */
+                              /* capacity (a serving step knows its longest sequence)  */
 } pa_multi_token_ext;
 
 /*
@@ -302,10 +306,11 @@ typedef struct pa_multi_token_ext {
  *   block_size    4, 8, 16 or 32;  scale  finite
  *
  * Device-side contract (not checked on the host, which never reads device memory):
- * n_s <= max_query_len and n_s <= L_s <= max_blocks_per_seq * bs, table entries in
- * use lie in [0, N).  A sequence whose query_start entries do not fit in [0, T] is
- * skipped; one with n_s > L_s or L_s > max_blocks_per_seq * bs, or a bad table entry,
- * gets NaN rows; rows past max_query_len are not written.
+ * n_s <= max_query_len and n_s <= L_s <= L_max, table entries in use lie in [0, N),
+ * where L_max = max_seq_len when it is set, else max_blocks_per_seq * bs.  A sequence
+ * whose query_start entries do not fit in [0, T] is skipped; one with n_s > L_s or
+ * L_s > L_max, or a bad table entry, gets NaN rows; rows past max_query_len are not
+ * written.
  *
  * Context split.  With few (sequence, KV head, 128-row tile) triples, e.g. a few draft
  * tokens per sequence over long contexts, one workgroup per triple leaves most of the
@@ -314,11 +319,11 @@ typedef struct pa_multi_token_ext {
  * sum, unnormalised output) into the workspace and combines them with log-sum-exp
  * weights in partition order in a second launch: deterministic, and equal to the
  * unsplit result up to fp32 rounding.  partition_size > 0 fixes part_tokens; 0 picks
- * it from the shapes alone (rows per tile, table capacity max_blocks_per_seq * bs,
- * the number of triples): a split only when there are fewer than 512 triples and
- * partitions of at least max(256, 16 * rows per tile) tokens, and then about 768
- * workgroups.  The automatic choice assumes sequences near the table's capacity;
- * callers that know shorter lengths pass partition_size.
+ * it from the shapes alone (rows per tile, L_max, the number of triples): a split only
+ * when there are fewer than 512 triples and partitions of at least max(256, 16 * rows
+ * per tile) tokens, and then about 768 workgroups.  Partitions past a sequence's
+ * length do no work, so the choice fits sequences near L_max: callers whose sequences
+ * are much shorter than the table's capacity set max_seq_len (or partition_size).
  *
  * Workspace (ext->workspace, ext->workspace_bytes): device memory owned by the
  * caller, of at least pa_multi_token_workspace_bytes bytes when the call splits (0
@@ -342,7 +347,7 @@ pa_status pa_multi_token(const void* q, const void* k_cache, const void* v_cache
  * pa_multi_token_workspace_bytes - bytes of workspace a pa_multi_token call with these
  * shapes needs: 0 when it does not split, else S * Hkv * tiles * parts * rows * (D + 2)
  * * 4, tiles = ceil(max_query_len * G / 128), rows = min(128, max_query_len * G),
- * parts = ceil(max_blocks_per_seq * bs / part_tokens).  Only the shape fields of ext
+ * parts = ceil(L_max / part_tokens).  Only the shape fields of ext
  * are read.  Returns PA_OK and sets *bytes, or the error status pa_multi_token would
  * report for the same shapes.
  */
@@ -394,7 +399,8 @@ const char* pa_last_error(void);
 /* ABI version of this header: bumped on any incompatible change. */
 int32_t pa_abi_version(void);
 
-#define PA_ABI_VERSION 3  /* 2: pa_decode_ext.shared_blocks; 3: pa_cache_write_decode */
+#define PA_ABI_VERSION 4  /* 2: pa_decode_ext.shared_blocks; 3: pa_cache_write_decode;
+                              4: pa_multi_token_ext.max_seq_len */
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,7 @@ from .build import LIB_PATH, INCLUDE
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_CAPACITY = range(6)
 PA_F32, PA_F16, PA_BF16 = range(3)
-ABI_VERSION = 3  # PA_ABI_VERSION of the header these structures mirror
+ABI_VERSION = 4  # PA_ABI_VERSION of the header these structures mirror
 TORCH_DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
 
@@ -48,7 +48,8 @@ class MultiTokenExt(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int64), ("partition_size", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p)]
+                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
+                ("max_seq_len", ctypes.c_int32)]
 
 
 class CopyBlocksExt(ctypes.Structure):
@@ -390,7 +391,7 @@ class PreparedMultiToken:
     def __init__(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  block_tables: torch.Tensor, seq_lens: torch.Tensor, query_start: torch.Tensor,
                  block_size: int, num_kv_heads: int, scale: float, out: torch.Tensor, *,
-                 max_query_len: int, partition_size: int = 0,
+                 max_query_len: int, partition_size: int = 0, max_seq_len: int = 0,
                  workspace: Optional[torch.Tensor] = None, stream=None):
         dev = q.device
         _need(dev.type == "cuda", "tensors must be on a GPU")
@@ -417,7 +418,7 @@ class PreparedMultiToken:
         ext = MultiTokenExt(num_seqs=S, num_tokens=T, max_query_len=max_query_len,
                             num_q_heads=Hq, head_dim=D, max_blocks_per_seq=block_tables.shape[1],
                             num_blocks=N, partition_size=partition_size,
-                            dtype=TORCH_DTYPE[q.dtype])
+                            dtype=TORCH_DTYPE[q.dtype], max_seq_len=max_seq_len)
         need = ctypes.c_size_t(0)
         _check(lib().pa_multi_token_workspace_bytes(ctypes.byref(ext), block_size, num_kv_heads,
                                                     ctypes.byref(need)), "pa_multi_token")
@@ -449,19 +450,21 @@ class PreparedMultiToken:
 def pa_multi_token(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                    block_tables: torch.Tensor, seq_lens: torch.Tensor, query_start: torch.Tensor,
                    block_size: int, num_kv_heads: int, scale: float, out: torch.Tensor, *,
-                   max_query_len: int, partition_size: int = 0,
+                   max_query_len: int, partition_size: int = 0, max_seq_len: int = 0,
                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Attention for several new tokens per sequence (see include/pa.h): q, out
     [T, Hq, D]; query_start int32 [S+1] on the GPU; ``max_query_len`` >= every
     sequence's number of new tokens (a host value: it sizes the launch).
     ``partition_size``: 0 splits the context automatically when the launch would be
-    small, < 0 never, > 0 into partitions of that many tokens.  A split call needs a
+    small, < 0 never, > 0 into partitions of that many tokens.  ``max_seq_len`` (a host
+    value, 0 = the table's capacity) bounds every length: the automatic split is sized
+    for it, and a longer sequence gets NaN rows.  A split call needs a
     byte tensor of ``pa_multi_token_workspace_bytes`` bytes (scratch, no zero-fill);
     when omitted, one is allocated for this call."""
     return PreparedMultiToken(q, k_cache, v_cache, block_tables, seq_lens, query_start,
                               block_size, num_kv_heads, scale, out,
                               max_query_len=max_query_len, partition_size=partition_size,
-                              workspace=workspace, stream=stream)()
+                              max_seq_len=max_seq_len, workspace=workspace, stream=stream)()
 
 
 class PreparedCopyBlocks:

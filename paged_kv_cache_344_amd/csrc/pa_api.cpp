@@ -152,7 +152,7 @@ pa_status decode_grid(int dtype, int D, int bs, int* grid) {
 // Shapes of a pa_multi_token call, checked, and its context split.
 struct MtPlan {
   bool empty = false;       // nothing to compute
-  int32_t max_tokens = 0;   // max_blocks_per_seq * bs
+  int32_t max_tokens = 0;   // L_max: max_seq_len if given, else max_blocks_per_seq * bs
   int32_t tiles = 0;        // 128-row tiles per (sequence, KV head)
   int32_t parts = 1;        // context partitions (1: no split)
   int32_t part_tokens = 0;  // positions per partition
@@ -178,8 +178,12 @@ pa_status plan_multi_token(const pa_multi_token_ext* ext, int32_t bs, int32_t hk
   if (MB <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d <= 0", MB);
   if (ext->num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks %lld <= 0", (long long)ext->num_blocks);
   if (!dtype_valid(ext->dtype)) return fail(PA_ERR_INVALID_ARG, "dtype %d", ext->dtype);
-  const int64_t max_tokens = (int64_t)MB * bs;
-  if (max_tokens > (int64_t(1) << 30)) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size too large");
+  if (ext->max_seq_len < 0) return fail(PA_ERR_INVALID_ARG, "max_seq_len %d < 0", ext->max_seq_len);
+  if ((int64_t)MB * bs > (int64_t(1) << 30)) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size too large");
+  // L_max: the caller's bound on every length when given (the split is sized for it and
+  // a longer sequence gets NaN rows), else what the table can hold
+  const int64_t max_tokens = ext->max_seq_len > 0 ? std::min<int64_t>(ext->max_seq_len, (int64_t)MB * bs)
+                                                  : (int64_t)MB * bs;
   const int32_t psz = ext->partition_size;
   if (psz > 0 && psz % 32) return fail(PA_ERR_INVALID_ARG, "partition_size %d is not a multiple of 32", psz);
   pl->max_tokens = (int32_t)max_tokens;

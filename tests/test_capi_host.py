@@ -284,6 +284,7 @@ def _mt(lib, ptr=FAKE, ext=True, scale=0.1, bs=16, hkv=8, **kw):
     (dict(num_seqs=70000), B.PA_ERR_INVALID_ARG),
     (dict(num_tokens=-1), B.PA_ERR_INVALID_ARG),
     (dict(max_query_len=-1), B.PA_ERR_INVALID_ARG),
+    (dict(max_seq_len=-1), B.PA_ERR_INVALID_ARG),
     (dict(num_q_heads=60), B.PA_ERR_INVALID_ARG),         # not a multiple of Hkv
     (dict(head_dim=96), B.PA_ERR_UNSUPPORTED),
     (dict(head_dim=0), B.PA_ERR_INVALID_ARG),
@@ -320,14 +321,14 @@ def _mt_ws(lib, bs=16, hkv=8, **kw):
     return st, n.value
 
 
-def _mt_expected(S, T, mq, Hq, Hkv, D, MB, bs, psz):
+def _mt_expected(S, T, mq, Hq, Hkv, D, MB, bs, psz, msl=0):
     """Workspace bytes of the documented context-split policy."""
     G = Hq // Hkv
     rows = min(mq, T) * G
     tiles = -(-rows // 128)
     part_rows = min(128, rows)
     triples = S * Hkv * tiles
-    max_tokens = MB * bs
+    max_tokens = min(msl, MB * bs) if msl > 0 else MB * bs
     if psz > 0:
         pt = psz
     elif psz < 0:
@@ -355,16 +356,24 @@ def _mt_expected(S, T, mq, Hq, Hkv, D, MB, bs, psz):
     dict(num_seqs=64, max_query_len=4, num_tokens=256, max_blocks_per_seq=2048),  # 512 triples
     dict(num_seqs=8, max_query_len=2, num_tokens=16, num_q_heads=8, max_blocks_per_seq=100,
          head_dim=64),                                       # G = 1, 2 rows per tile
+    dict(num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=8192,
+         max_seq_len=20000),                                 # split sized from the bound
+    dict(num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=2048,
+         max_seq_len=1 << 20),                               # bound above capacity: capacity
+    dict(num_seqs=2, max_query_len=4, num_tokens=8, max_blocks_per_seq=2048,
+         max_seq_len=300),                                   # too short to split
 ])
 def test_multi_token_workspace_formula(lib, kw):
     st, n = _mt_ws(lib, **kw)
     assert st == B.PA_OK
-    a = dict(S=4, T=64, mq=32, Hq=64, D=128, MB=64, psz=0)
+    a = dict(S=4, T=64, mq=32, Hq=64, D=128, MB=64, psz=0, msl=0)
     names = dict(num_seqs="S", num_tokens="T", max_query_len="mq", num_q_heads="Hq",
-                 head_dim="D", max_blocks_per_seq="MB", partition_size="psz")
+                 head_dim="D", max_blocks_per_seq="MB", partition_size="psz",
+                 max_seq_len="msl")
     for k, v in kw.items():
         a[names[k]] = v
-    want = _mt_expected(a["S"], a["T"], a["mq"], a["Hq"], 8, a["D"], a["MB"], 16, a["psz"])
+    want = _mt_expected(a["S"], a["T"], a["mq"], a["Hq"], 8, a["D"], a["MB"], 16, a["psz"],
+                        a["msl"])
     assert n == want
 
 

@@ -40,18 +40,19 @@ class Mt:
         self.out = torch.empty_like(self.q)
 
     def run(self, seq_lens=None, block_tables=None, qs=None, max_q=None, partition_size=-1,
-            workspace=None):
+            workspace=None, max_seq_len=0):
         b = self.b
         say(f"pa_multi_token {b.name} seed={b.seed} {b.dtype} S={b.num_seqs} T={self.q.shape[0]} "
             f"Hq={b.num_q_heads} Hkv={b.num_kv_heads} D={b.head_dim} bs={b.block_size} "
-            f"partition_size={partition_size}")
+            f"partition_size={partition_size} max_seq_len={max_seq_len}")
         call = pa.PreparedMultiToken(self.q, self.k_cache, self.v_cache,
                                      self.block_tables if block_tables is None else block_tables,
                                      self.seq_lens if seq_lens is None else seq_lens,
                                      self.qs if qs is None else qs, b.block_size, b.num_kv_heads,
                                      b.scale, self.out,
                                      max_query_len=self.max_q if max_q is None else max_q,
-                                     partition_size=partition_size, workspace=workspace)
+                                     partition_size=partition_size, max_seq_len=max_seq_len,
+                                     workspace=workspace)
         self.workspace_bytes = call.workspace_bytes
         call()
         torch.cuda.synchronize()
@@ -217,6 +218,30 @@ def test_split_automatic_verify(dtype):
     got = g.run(partition_size=0)
     assert g.workspace_bytes > 0
     check_close(got, _oracle(b), dtype, f"automatic split verify {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_split_sized_from_max_seq_len(dtype):
+    """A table 16 times wider than the sequences (as when a pool is sized for the longest
+    request a server admits): with max_seq_len the automatic split is sized from the
+    stated bound instead of the capacity, so it cuts these sequences into more
+    partitions; both agree with the oracle, and a sequence longer than the bound gets
+    NaN rows while the others stay exact."""
+    lens, new = [3000, 1700, 2900, 1000], [5, 5, 4, 5]
+    b = inputs.make_batch("gqa_bf16", seed=16, dtype=dtype, num_seqs=4, lens=("fixed", lens),
+                          new_tokens=new, max_blocks_per_seq=3072, cache_write=False)
+    ref = _oracle(b)
+    g = Mt(b)
+    wide = g.run(partition_size=0)
+    ws_wide = g.workspace_bytes
+    check_close(wide, ref, dtype, f"split sized from the capacity {dtype}")
+    tight = g.run(partition_size=0, max_seq_len=max(lens))
+    assert g.workspace_bytes > 0 and g.workspace_bytes != ws_wide
+    check_close(tight, ref, dtype, f"split sized from max_seq_len {dtype}")
+    got = g.run(partition_size=0, max_seq_len=2950)     # sequence 0 (3000) is longer
+    qs = b.query_start
+    assert np.isnan(got[qs[0]:qs[1]]).all()
+    check_close(got[qs[1]:], ref[qs[1]:], dtype, f"sequences within max_seq_len {dtype}")
 
 
 def test_split_contract_violations():
