@@ -99,14 +99,24 @@ def test_parity_long_chunks(gain):
 
 
 def test_full_size_prefill_sampled():
-    """The chunked-prefill batch at full size (8 sequences, 512 new tokens on 1024-8192
-    cached, GQA-8): sampled rows against the oracle, each computed as the decode of the
-    sequence cut just after that token (the causal definition)."""
+    """The chunked-prefill batch the benchmark times, at full size (8 sequences, 512 new
+    tokens on 1024-8192 cached, GQA-8): every output of the sequences with the longest
+    and the shortest context against the oracle, and sampled rows of every sequence,
+    each computed as the decode of the sequence cut just after that token (the causal
+    definition)."""
     b = inputs.make_batch("prefill_bf16", seed=0)
     got = Mt(b).run()
     assert np.isfinite(got).all()
-    rng = np.random.default_rng(0)
     qs = b.query_start
+    ctxs = b.seq_lens - np.diff(qs)
+    for s in sorted({int(np.argmax(ctxs)), int(np.argmin(ctxs))}):
+        sub_qs = np.array([0, qs[s + 1] - qs[s]], np.int32)
+        want = oracle.multi_token(b.q[qs[s]:qs[s + 1]], b.k_cache, b.v_cache,
+                                  b.block_tables[s:s + 1], b.seq_lens[s:s + 1], sub_qs,
+                                  b.block_size, b.num_kv_heads, b.scale, b.dtype)
+        rep = check_close(got[qs[s]:qs[s + 1]], want, "bf16", f"prefill every output of s={s}")
+        say(f"prefill s={s} (context {int(ctxs[s])}) every output: {rep}")
+    rng = np.random.default_rng(0)
     for s in range(b.num_seqs):
         n = int(qs[s + 1] - qs[s])
         ctx = int(b.seq_lens[s]) - n
