@@ -476,7 +476,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this library "
-              "runs its hot path on a single MI355X; see DESIGN.md for how it would shard)",
+              "runs its hot path on a single MI355X)",
               file=sys.stderr)
         return 2
 
