@@ -1,0 +1,111 @@
+"""Host logic of bench.py, on the CPU: the algorithmic byte and flop counts behind every
+roofline figure, checked against a brute-force enumeration of what each call must read,
+write or compute; the source digest that ties the committed traffic counters to the
+kernel code; the parity rule; and the refusal of more than one GPU."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+from paged_kv_cache_344_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _rows_read(b):
+    """Distinct physical (block, slot) positions the batch attends: shared blocks once."""
+    seen = set()
+    for s in range(b.num_seqs):
+        for t in range(int(b.seq_lens[s])):
+            seen.add((int(b.block_tables[s, t // b.block_size]), t % b.block_size))
+    return len(seen)
+
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny_fp32", {}),
+    ("gqa_bf16", dict(num_seqs=6, lens=("fixed", [1, 15, 16, 17, 100, 333]), max_blocks_per_seq=30)),
+    ("prefix_bf16", dict(num_seqs=5, max_blocks_per_seq=200)),
+])
+def test_decode_bytes_by_enumeration(name, over):
+    b = inputs.make_batch(name, 1, **over)
+    e = bench.elem_bytes(b.dtype)
+    kv = 2 * b.num_kv_heads * b.head_dim * e               # K and V of one position, all KV heads
+    qo = 2 * b.num_seqs * b.num_q_heads * b.head_dim * e    # queries read, outputs written
+    tables = 4 * sum(-(-int(L) // b.block_size) for L in b.seq_lens)
+    want = _rows_read(b) * kv + qo + tables + 4 * b.num_seqs
+    assert bench.decode_bytes(b) == want
+    if b.shared_blocks:  # as if nothing were shared: every table's positions
+        want_logical = int(b.seq_lens.sum()) * kv + qo + tables + 4 * b.num_seqs
+        assert bench.decode_bytes(b, unique_shared=False) == want_logical
+        assert want_logical > want
+
+
+def test_cache_write_bytes_by_enumeration():
+    b = inputs.make_batch("gqa_bf16", 2, num_seqs=7, lens=("fixed", [3, 9, 16, 17, 40, 64, 1]),
+                          max_blocks_per_seq=8)
+    e = bench.elem_bytes(b.dtype)
+    per_token = 0
+    for _ in range(b.num_kv_heads):
+        per_token += 2 * b.head_dim * e      # read the new K and V rows
+        per_token += 2 * b.head_dim * e      # write them into the pools
+    want = b.slot_mapping.shape[0] * (per_token + 8)  # plus the int64 slot
+    assert bench.cache_write_bytes(b) == want
+
+
+def test_multi_token_counts_by_enumeration():
+    b = inputs.make_batch("gqa_bf16", 3, num_seqs=4, lens=("fixed", [5, 40, 33, 100]),
+                          new_tokens=[5, 8, 1, 30], max_blocks_per_seq=10, cache_write=False)
+    qs = b.query_start
+    flops = 0
+    for s in range(b.num_seqs):
+        n = int(qs[s + 1] - qs[s])
+        ctx = int(b.seq_lens[s]) - n
+        for j in range(n):                   # new token j sees positions 0 .. ctx + j
+            for _pos in range(ctx + j + 1):
+                flops += b.num_q_heads * 4 * b.head_dim
+    assert bench.multi_token_flops(b) == flops
+    e = bench.elem_bytes(b.dtype)
+    T = int(qs[-1])
+    want = (_rows_read(b) * 2 * b.num_kv_heads * b.head_dim * e + 2 * T * b.num_q_heads * b.head_dim * e
+            + 4 * sum(-(-int(L) // b.block_size) for L in b.seq_lens) + 4 * b.num_seqs + 4 * (b.num_seqs + 1))
+    assert bench.multi_token_bytes(b) == want
+
+
+def test_source_digest_follows_code_only():
+    code = "int a = 1;\n// a comment\n#ifdef PA_DECODE_TRACE\nint tr = 2;\n#endif\nint b = a;\n"
+    base = bench._product_code(code)
+    assert base == bench._product_code(code.replace("// a comment", "// another comment"))
+    assert base == bench._product_code(code.replace("int tr = 2;", "int tr = 3;\nint more;"))
+    assert base != bench._product_code(code.replace("int b = a;", "int b = a + 1;"))
+    assert "tr" not in base and "comment" not in base
+
+
+def test_traffic_record_is_used_only_for_the_profiled_code(monkeypatch):
+    rec = bench.measured_traffic("gqa_bf16/pa_cache_write_decode", 0)
+    assert rec is None or rec > 3.5e8        # committed counters for the present code
+    monkeypatch.setattr(bench, "source_digest", lambda: "not the profiled code")
+    assert bench.measured_traffic("gqa_bf16/pa_cache_write_decode", 0) is None
+    assert bench.measured_traffic("no such kernel", 0) is None
+
+
+def test_parity_rule():
+    rng = np.random.default_rng(4)
+    ref = rng.standard_normal((3, 4, 128)) * 0.01
+    exact = torch.from_numpy(ref).to(torch.bfloat16)          # rounded once: within the bound
+    assert bench.parity(exact, ref, "bf16")["ok"]
+    bad = exact.double().numpy().copy()
+    bad[1, 2, 5] += 0.05 * np.sqrt(np.mean(ref[1, 2] ** 2)) + 1e-4   # far beyond ulp + rms/1024
+    r = bench.parity(torch.from_numpy(bad), ref, "bf16")
+    assert r["max_over_ulp_rms_bound"] > 1 and not r["ok"]
+    assert bench.parity(torch.from_numpy(ref.copy()), ref, "f32")["ok"]
+    assert not bench.parity(torch.from_numpy(ref + 1e-4), ref, "f32")["ok"]
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
