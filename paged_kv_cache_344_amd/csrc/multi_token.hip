@@ -37,14 +37,18 @@
 // masked, and their values are cleared in LDS before the weighted sum.
 //
 // Precision.  Products accumulate in fp32.  The softmax weights enter the second product
-// as a hi + lo pair for bf16 (its 8 significant bits alone would show next to the
-// output's own rounding), rounded once for fp16, and exactly for fp32; the sum that
-// normalises them is kept in fp32.
+// as a hi + lo pair of the 16-bit input type (8 or 11 significant bits alone would show
+// next to the output's own rounding: a weight's rounding error reaches the output at
+// the scale of the values, while averaging can make the output much smaller), and
+// exactly for fp32; the sum that normalises them is kept in fp32.  Each row's exponent
+// base moves only when a logit exceeds it by more than kLazyRescale, so weights lie in
+// [0, 2^8] rather than [0, 1]: the same relative precision, and most chunks skip the
+// rescale of the accumulators (FlashAttention-4's conditional rescaling).
 //
 // Context split.  With few (row tile, KV head, sequence) triples, as when a few draft
 // tokens per sequence are verified against long contexts, the tokens of each sequence
 // are cut into partitions of part_tokens positions, one workgroup each; every
-// workgroup leaves its rows' running maximum, sum and unnormalised output in a
+// workgroup leaves its rows' exponent base, sum and unnormalised output in a
 // workspace, and a second launch combines them with log-sum-exp weights.
 //
 // Launch.  One workgroup per (row tile, partition, KV head, sequence).  Workgroups are
@@ -75,6 +79,10 @@ constexpr int NTILE = 2;                    // 16-row MFMA tiles per wave
 constexpr int ROWS = WAVES * NTILE * 16;    // rows of one workgroup
 constexpr int CH = 32;                      // tokens per chunk
 constexpr int XCDS = 8;
+// Lazy rescaling (log2 units): the exponent base of a row moves only when a logit
+// exceeds it by more than this, so weights stay below 2^8 and most chunks skip the
+// rescale of the accumulators
+constexpr float kLazyRescale = 8.f;
 
 template <typename T>
 struct V8;
@@ -128,12 +136,30 @@ __device__ __forceinline__ float max8(const float (&z)[8]) {
   return m;
 }
 
+// Lazy rescaling of one row tile for one chunk.  lm is this lane's largest logit of the
+// chunk in log2 units (the four lanes of a row share the row's base).  Only when some
+// row of the wave has a logit above its base + kLazyRescale is the row maximum formed;
+// such a row's base moves to it and what the row summed so far shrinks by
+// exp2(old - new), while the other rows get exp2(0) = 1.
+template <int NT>
+__device__ __forceinline__ void rebase(float lm, float& m_base, float& l_run, f32x4 (&acc)[NT]) {
+  if (__any(lm > m_base + kLazyRescale)) {
+    const float cm = max_over_quads(lm);
+    const float mb = cm > m_base + kLazyRescale ? cm : m_base;
+    const float alpha = exp2_fast(m_base - mb);
+    l_run *= alpha;
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn) acc[nn] *= alpha;
+    m_base = mb;
+  }
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// eight weights as MFMA operands of a 16-bit type: hi = nearest T, and (bf16 only)
-// lo = nearest T to the remainder, converted two at a time
+// eight weights as MFMA operands of a 16-bit type: hi = nearest T, lo = nearest T to
+// the remainder, converted two at a time
 template <typename T>
 __device__ __forceinline__ void split_weights(const float (&p)[8], u32x4& hi, u32x4& lo) {
   typedef typename std::conditional<std::is_same<T, __bf16>::value, bf16x2, f16x2>::type T2;
@@ -141,12 +167,15 @@ __device__ __forceinline__ void split_weights(const float (&p)[8], u32x4& hi, u3
   for (int k = 0; k < 4; ++k) {
     const T2 h = __builtin_convertvector((f32x2){p[2 * k], p[2 * k + 1]}, T2);
     hi[k] = __builtin_bit_cast(uint32_t, h);
+    f32x2 w;  // hi, widened exactly
     if constexpr (std::is_same<T, __bf16>::value) {
-      // a bf16 is the upper half of an fp32: widen both halves exactly, take the rest
-      const float h0 = __uint_as_float(hi[k] << 16), h1 = __uint_as_float(hi[k] & 0xFFFF0000u);
-      const T2 l = __builtin_convertvector((f32x2){p[2 * k] - h0, p[2 * k + 1] - h1}, T2);
-      lo[k] = __builtin_bit_cast(uint32_t, l);
+      // a bf16 is the upper half of an fp32
+      w = f32x2{__uint_as_float(hi[k] << 16), __uint_as_float(hi[k] & 0xFFFF0000u)};
+    } else {
+      w = __builtin_convertvector(h, f32x2);
     }
+    const T2 l = __builtin_convertvector((f32x2){p[2 * k] - w[0], p[2 * k + 1] - w[1]}, T2);
+    lo[k] = __builtin_bit_cast(uint32_t, l);
   }
 }
 
@@ -429,11 +458,14 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? (ONE_TILE ? 2 : 3) : 1) v
     }
   };
 
-  float m_run[NTILE], l_run[NTILE];
+  // per row: the exponent base and the running sum of the weights against it.  Until
+  // the row sees a position the base is -FLT_MAX: the first finite logit moves it (its
+  // rescale factor exp2(-FLT_MAX - m) is 0), and masked logits still give exp2(-inf) = 0
+  float m_base[NTILE], l_run[NTILE];
   f32x4 acc[NTILE][NT];
 #pragma unroll
   for (int t = 0; t < NTILE; ++t) {
-    m_run[t] = -INFINITY;
+    m_base[t] = -FLT_MAX;
     l_run[t] = 0.f;
 #pragma unroll
     for (int nn = 0; nn < NT; ++nn) acc[t][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -455,6 +487,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? (ONE_TILE ? 2 : 3) : 1) v
     // key rows col (tile a) and 16 + col (tile b) share their swizzle
     const T* ka = &sk[buf][col * KSEG * EPL];
     const T* kb = ka + 16 * KSEG * EPL;
+    if constexpr (ALL) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int k = 0; k < KL; ++k) {
       const int seg = (4 * k + quad) ^ kswz<KSEG>(col);
@@ -478,16 +511,18 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? (ONE_TILE ? 2 : 3) : 1) v
         }
       }
     }
+    if constexpr (ALL) __builtin_amdgcn_s_setprio(0);
     // per row tile: softmax of the chunk, then its weighted sum
     const int tfirst = t0 + 8 * quad;
     // dimension 16nn + col, tokens 8quad .. 8quad + 7: value segment quad (two for fp32)
     const T* vrow = &sv[buf][(8 / TPS) * quad * D * TPS + col * TPS];
     if constexpr (ALL) {
       // Both tiles; masking first, on the logits (a masked logit is -inf, so its
-      // weight is exp2(-inf) = 0 with no second select); then tile 0's softmax and
-      // rescale, tile 1's softmax, tile 0's weighted sum, tile 1's rescale and weighted
-      // sum.  Per tile the operations and their order are those of the loop below, so
-      // the results are the same bits.
+      // weight is exp2(-inf) = 0 with no second select); then both softmaxes, then both
+      // weighted sums.  Per tile the operations and their order are those of the loop
+      // below, so the results are the same bits.  The waves raise their priority while
+      // they issue MFMAs, so that a wave with matrix work ready issues it ahead of
+      // another wave's vector work (measured 1% faster on chunked prefill).
       typedef typename V8<T>::type VT;
       static_assert(NTILE == 2, "two row tiles a wave");
       if (masked) {
@@ -506,40 +541,30 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? (ONE_TILE ? 2 : 3) : 1) v
           z[e] = sa[t][e];
           z[4 + e] = sb[t][e];
         }
-        const float cm = max_over_quads(max8(z));
-        const float m_new = fmaxf(m_run[t], cm * sc);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2_fast(m_run[t] - m_use);
-        float pr[8], psum = 0.f;
+        rebase(max8(z) * sc, m_base[t], l_run[t], acc[t]);
+        float pr[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(__builtin_fmaf(z[e], sc, -m_use));
+        for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(__builtin_fmaf(z[e], sc, -m_base[t]));
+        float psum = pr[0];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) psum += pr[e];
-        l_run[t] = l_run[t] * alpha + psum;
-        m_run[t] = m_new;
+        for (int e = 1; e < 8; ++e) psum += pr[e];
+        l_run[t] += psum;
         split_weights<T>(pr, hi, lo);
-        return alpha;
-      };
-      auto rescale = [&](int t, float alpha) {
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int nn = 0; nn < NT; ++nn) acc[t][nn] *= alpha;
-        }
       };
       auto weighted_sum = [&](int t, const u32x4& hi, const u32x4& lo) {
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int nn = 0; nn < NT; ++nn) {
           const VT vv = *reinterpret_cast<const VT*>(vrow + 16 * nn * TPS);
           acc[t][nn] = mma16(vv, __builtin_bit_cast(VT, hi), acc[t][nn]);
-          if constexpr (std::is_same<T, __bf16>::value)
-            acc[t][nn] = mma16(vv, __builtin_bit_cast(VT, lo), acc[t][nn]);
+          acc[t][nn] = mma16(vv, __builtin_bit_cast(VT, lo), acc[t][nn]);
         }
+        __builtin_amdgcn_s_setprio(0);
       };
       u32x4 h0, l0, h1, l1;
-      rescale(0, softmax(0, h0, l0));
-      const float a1 = softmax(1, h1, l1);
+      softmax(0, h0, l0);
+      softmax(1, h1, l1);
       weighted_sum(0, h0, l0);
-      rescale(1, a1);
       // tile 1 reads the value operands again rather than keeping tile 0's live
       uint32_t vaddr = (uint32_t)(uintptr_t)(lds_void*)vrow;
       asm volatile("" : "+v"(vaddr));
@@ -560,35 +585,23 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? (ONE_TILE ? 2 : 3) : 1) v
 #pragma unroll
         for (int e = 0; e < 8; ++e) z[e] = (tfirst + e <= lim[t]) ? z[e] : -INFINITY;
       }
-      const float cm = max_over_quads(max8(z));
-      // a row with every position of this chunk masked keeps its maximum (max(m, -inf)
-      // = m); while it has seen no position at all (a partition that starts past its
-      // causal limit) the maximum stays -inf and is taken as 0 in the exponents, so that
-      // its weights and rescale factor are exp2(-inf) = 0, never exp2(-inf + inf)
-      const float m_new = fmaxf(m_run[t], cm * sc);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run[t] - m_use);
-      float pr[8], psum = 0.f;
+      // a row with every position of this chunk masked has maximum -inf here and keeps
+      // its base (a partition that starts past a row's causal limit leaves it at -FLT_MAX)
+      rebase(max8(z) * sc, m_base[t], l_run[t], acc[t]);
+      float pr[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(__builtin_fmaf(z[e], sc, -m_use));
+      for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(__builtin_fmaf(z[e], sc, -m_base[t]));
       if (masked) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) pr[e] = (tfirst + e <= lim[t]) ? pr[e] : 0.f;
       }
+      float psum = pr[0];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) psum += pr[e];
-      l_run[t] = l_run[t] * alpha + psum;
-      m_run[t] = m_new;
-      // after the first chunks the running maximum rarely moves: rescale only when it
-      // moved for some row of this wave
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int nn = 0; nn < NT; ++nn) acc[t][nn] *= alpha;
-      }
+      for (int e = 1; e < 8; ++e) psum += pr[e];
+      l_run[t] += psum;
       if constexpr (sizeof(T) == 2) {
-        // bf16 keeps 8 significant bits: the weights go in as a hi + lo pair (two
-        // MFMAs), about fp32 accuracy, so that the output's own rounding is the only
-        // visible error; fp16's 11 bits need one rounding only
+        // the weights go in as a hi + lo pair (two MFMAs), about fp32 accuracy, so that
+        // the output's own rounding is the only visible error
         typedef typename V8<T>::type VT;
         u32x4 phi, plo;
         split_weights<T>(pr, phi, plo);
@@ -596,8 +609,7 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? (ONE_TILE ? 2 : 3) : 1) v
         for (int nn = 0; nn < NT; ++nn) {
           const VT vv = *reinterpret_cast<const VT*>(vrow + 16 * nn * TPS);
           acc[t][nn] = mma16(vv, __builtin_bit_cast(VT, phi), acc[t][nn]);
-          if constexpr (std::is_same<T, __bf16>::value)
-            acc[t][nn] = mma16(vv, __builtin_bit_cast(VT, plo), acc[t][nn]);
+          acc[t][nn] = mma16(vv, __builtin_bit_cast(VT, plo), acc[t][nn]);
         }
       } else {
 #pragma unroll
@@ -661,8 +673,9 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? (ONE_TILE ? 2 : 3) : 1) v
   bad = __syncthreads_or(bad);
 
   if (split) {
-    // this partition's partial rows for the merge: running maximum (log2 units), sum
-    // and unnormalised output; a bad table entry makes them NaN
+    // this partition's partial rows for the merge: exponent base (log2 units; -inf for a
+    // row that saw no position), sum and unnormalised output; a bad table entry makes
+    // them NaN
     const int64_t tile0 =
         ((((int64_t)s * P.num_kv_heads + g) * P.row_tiles + x) * P.parts + part) * P.part_rows;
     const float nan = __builtin_nanf("");
@@ -675,8 +688,9 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? (ONE_TILE ? 2 : 3) : 1) v
 #pragma unroll
       for (int nn = 0; nn < NT; ++nn)
         *reinterpret_cast<f32x4*>(po + 16 * nn) = bad ? f32x4{nan, nan, nan, nan} : acc[t][nn];
+      const float mb = m_base[t] == -FLT_MAX ? -INFINITY : m_base[t];
       if (quad == 0)
-        *reinterpret_cast<f32x2*>(P.part_ml + 2 * r) = bad ? f32x2{nan, nan} : f32x2{m_run[t], l};
+        *reinterpret_cast<f32x2*>(P.part_ml + 2 * r) = bad ? f32x2{nan, nan} : f32x2{mb, l};
     }
     return;
   }
