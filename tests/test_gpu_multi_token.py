@@ -187,6 +187,58 @@ def test_contract_violations():
     check_close(got[:qs[2]], ref[:qs[2]], "bf16", "multi_token before the skipped ones")
 
 
+# Logit profiles along the context, in log2 units (position t): the kernel moves a row's
+# exponent base only when a logit passes it by more than 8, so these make the base move
+# at every jump (steps of 12), every few chunks (a slow ramp), never after the first
+# chunk (jumps of 7.5 that come and go), or at every chunk over a range of hundreds
+# (weights of the early positions underflow to 0, as they do in the oracle's fp64).
+MOVING = {
+    "steps": lambda t: 12.0 * (t // 64) - 50.0,
+    "ramp": lambda t: 0.06 * t,
+    "below": lambda t: 7.5 * ((t // 32) % 2) + 0.001 * t,
+    "wide": lambda t: 0.5 * t - 300.0,
+}
+
+
+def _moving_base_batch(profile, dtype, seed):
+    """Every query row is A u and every cached key of position t is c(t) u for one unit
+    vector u, so that each row's logit at t is the profile's value (the values stay
+    random)."""
+    lens, new = [700, 1200, 333, 64], [300, 100, 33, 64]
+    b = inputs.make_batch("gqa_bf16", seed=seed, dtype=dtype, num_q_heads=16, num_kv_heads=2,
+                          num_seqs=4, lens=("fixed", lens), new_tokens=new,
+                          max_blocks_per_seq=80, cache_write=False)
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(b.head_dim)
+    u /= np.linalg.norm(u)
+    A = 4.0
+    b.q = inputs.to_storage(np.broadcast_to(A * u, b.q.shape).astype(np.float32), dtype)
+    for s, L in enumerate(lens):
+        t = np.arange(L)
+        c = MOVING[profile](t) / (b.scale * A * np.log2(np.e))
+        rows = inputs.to_storage((c[:, None] * u[None, :]).astype(np.float32), dtype)
+        blk = b.block_tables[s, t // b.block_size]
+        for g in range(b.num_kv_heads):
+            b.k_cache[blk, g, t % b.block_size, :] = rows
+    return b
+
+
+# fp32 runs every profile but "wide": there the logits that carry the weight lie 270-300
+# log2 units from zero, and an fp32 dot product of that size is off by about
+# 2^-24 |q| |k|, which moves the weights by more than the 1e-5 fp32 bound allows (8e-5
+# measured); only the oracle's fp64 resolves them.
+@pytest.mark.parametrize("profile,dtype", [(p, d) for d in ("bf16", "f16", "f32")
+                                           for p in sorted(MOVING) if (p, d) != ("wide", "f32")])
+def test_parity_moving_base(profile, dtype):
+    """Logits that climb along the context, so that the exponent base moves (or just
+    does not) by known amounts, whole and split into 256-position partitions."""
+    b = _moving_base_batch(profile, dtype, seed=21)
+    g = Mt(b)
+    ref = _oracle(b)
+    check_close(g.run(), ref, dtype, f"moving base {profile} {dtype}")
+    check_close(g.run(partition_size=256), ref, dtype, f"moving base {profile} {dtype} split 256")
+
+
 # ---- context split: partitions of the positions, merged with log-sum-exp weights
 
 @pytest.mark.parametrize("psz", [32, 64, 96, 128])
