@@ -76,10 +76,10 @@ typedef struct pa_decode_ext {
   int32_t max_blocks_per_seq; /* row stride of block_tables, >= 1                      */
   int64_t num_blocks;         /* N, physical blocks in the pool, >= 1                  */
   int32_t partition_size;     /* tokens per split-K partition: 0 = default (chosen on  */
-                              /* the device from the lengths: 3/4 of one workgroup's */
-                              /* even share of the work, to the nearest 256, at least */
-                              /* 512), < 0 = never split, > 0 = that many (a multiple */
-                              /* of 32)                                               */
+                              /* the device from the lengths: one workgroup's even   */
+                              /* share of the work, rounded up to a multiple of 256,  */
+                              /* at least 512), < 0 = never split, > 0 = that many    */
+                              /* (a multiple of 32)                                    */
   int32_t dtype;              /* pa_dtype of q, k_cache, v_cache and out               */
   void* workspace;            /* device scratch: queue, counters, split-K partials;    */
                               /* caller-owned, zero-filled before first use            */

@@ -200,8 +200,8 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   // partition length is chosen first, from the lengths: every item ends with a merge
   // and, when split, partial results to write and merge later, which costs about as
   // much per item whatever its length, so partitions are made as long as the load
-  // balance allows, a fixed fraction (kPartShare) of one workgroup's even share of all
-  // the (token, KV head tile) work, to the nearest 256 tokens, never below part_tokens.
+  // balance allows: kPartShare times one workgroup's even share of all the (token, KV
+  // head tile) work, rounded up to a multiple of 256 tokens, never below part_tokens.
   // Every workgroup computes the same sum in the same order, so all choose alike.
   // Then: the number of full partitions of each sequence and the class of its last one
   // (0: an empty or invalid sequence, a one-item fill; 1: one chunk; 2 ..
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       for (int w = 0; w < NW; ++w) tot += sm_wsumf[w];
       const float share = tot * (float)HT2 / (float)gridDim.x;  // tokens per workgroup
       const float want = fminf(kPartShare * share, (float)P.max_tokens);
-      PT = max(PT, ((int)want + 128) / 256 * 256);  // nearest multiple of 256
+      PT = max(PT, (int)ceilf(want * (1.f / 256.f)) * 256);
     }
 #ifdef PA_DECODE_TRACE
     if (threadIdx.x == 0) tr[248] = PA_TRACE_STAMP();

@@ -11,7 +11,7 @@ constexpr int kScanMax = 1024;      // sequences one decode launch plans for (ho
 constexpr int kMergeFan = 16;       // partials combined per merge node
 constexpr int kMaxPartitions = 8192;
 constexpr int kSizeClasses = 17;    // classes the last partitions are ordered by
-constexpr float kPartShare = 0.75f;  // default partition: this fraction of a workgroup's share
+constexpr float kPartShare = 1.0f;  // default partition: this fraction of a workgroup's share
 constexpr size_t kStaticScratchBytes = size_t(64) << 20;  // pa_decode_noalloc's device scratch
 constexpr int kPartSlot = 16;       // int32 slot of the decode workspace header (byte 64) that
                                     // records the partition length the last launch used

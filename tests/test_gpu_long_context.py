@@ -89,11 +89,13 @@ def _place_needles(b, spots_by_seq, c=96.0):
 
 @pytest.mark.parametrize("bs", [16, 32])
 def test_long_context_needles_at_every_merge_position(bs):
-    """Two sequences of 131,072 and 100,001 tokens.  Sequence 0 carries needles placed
+    """Two sequences of 65,537 and 131,072 tokens.  Sequence 0 carries needles placed
     for 512-token partitions, sequence 1 for the default partition length (read back
-    from the device); both partitionings are decoded and every needle must be found."""
+    from the device: one workgroup's share, 3328 tokens here, so 40 partitions, the last
+    one ragged, reaching merge group 2); both partitionings are decoded and every needle
+    must be found."""
     name = "long_bf16_bs16" if bs == 16 else "long_bf16_bs32"
-    lens = [131072, 100001]
+    lens = [65537, 131072]
     b = inputs.make_batch(name, seed=43, num_seqs=2, lens=("fixed", lens), cache_write=False)
     g0 = OnGpu(b)
     _, p_default = _decode(g0, 0)

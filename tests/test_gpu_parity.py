@@ -435,8 +435,8 @@ def test_many_one_chunk_partitions_parity_and_repeats():
 
 def test_default_partitioning_lengthens_partitions():
     """With the default partition size the kernel sizes partitions from the lengths (here
-    142,924 tokens x 8 KV heads over 2 x 256 workgroups at bf16, head dim 128: 1792-token
-    partitions: 23 for the longest sequence, in two merge groups, and one for the
+    142,924 tokens x 8 KV heads over 2 x 256 workgroups at bf16, head dim 128: 2304-token
+    partitions: 18 for the longest sequence, in two merge groups, and one for the
     sequences of 1, 513 and 1025 tokens).  That and explicit 512-token
     partitions both match the oracle, and repeated default calls give the same bits."""
     lens = [40000, 35000, 30000, 16385, 1, 513, 1025, 20000]

@@ -10,7 +10,8 @@ tests/helpers.faithful_bound) must:
   * accept the exact result rounded to bf16 (what a correct kernel returns), and
   * reject the exact result of the same attention with one partition's tokens
     removed, one merge group of 16 partitions removed, one partition counted twice,
-    or one default-size partition (6144 tokens at this length) removed.
+    or one partition of the size the default rule picks for the long-context batch
+    (8448 tokens) removed.
 The altered results come from the oracle itself, run on block tables that leave out
 or repeat the partition's blocks: exactly what a merge that loses or doubles a
 partial would compute."""
@@ -58,7 +59,7 @@ def test_rounded_exact_result_passes(long_seq):
 @pytest.mark.parametrize("case", ["drop partition 100 (512 tokens)",
                                   "drop merge group 2 (16 x 512 tokens)",
                                   "count partition 100 twice",
-                                  "drop default partition 7 (6144 tokens)"])
+                                  "drop default partition 7 (8448 tokens)"])
 def test_lost_or_doubled_work_is_rejected(long_seq, case):
     b, ref = long_seq
     row = list(b.block_tables[0, :L // BS])
@@ -70,7 +71,7 @@ def test_lost_or_doubled_work_is_rejected(long_seq, case):
     elif case.startswith("count"):
         keep = row + row[100 * per:101 * per]
     else:
-        dper = 6144 // BS
+        dper = 8448 // BS
         keep = row[:7 * dper] + row[8 * dper:]
     bad = _bf16(_altered(b, keep))
     d = np.abs(bad - ref)
