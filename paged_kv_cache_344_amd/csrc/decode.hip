@@ -659,8 +659,10 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
                 const uint32_t h = (word >> (16 * (d & 1))) & 0xFFFFu;
                 const uint32_t x = c.v[nn][0][e >> 1];
                 c.v[nn][0][e >> 1] = (e & 1) ? ((x & 0x0000FFFFu) | (h << 16)) : ((x & 0xFFFF0000u) | h);
-              } else {
-                c.v[nn][e >> 2][e & 3] = word;
+              } else {  // a static index, so that the chunk buffer stays in registers
+#pragma unroll
+                for (int x = 0; x < 8; ++x)
+                  if (x == e) c.v[nn][x >> 2][x & 3] = word;
               }
             }
           }
@@ -733,14 +735,22 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
 #ifdef PA_DECODE_TRACE
       tr_il = PA_TRACE_STAMP();
 #endif
+      // the epilogue's per-lane indices.  In the fused instance they are recomputed
+      // here from an opaque copy of the thread index: hoisted out of the item loop they
+      // would be held across the chunk loop, which then spills (measured 1.3% on the
+      // fused step; the other instances fit and keep the hoisted form, which measured
+      // the same or up to 1.5% faster for them)
+      int etid = tid;
+      if constexpr (FUSE) asm volatile("" : "+v"(etid));
+      const int elane = etid & 63, ecol = elane & 15, equad = elane >> 4;
       if (tiny) {
         // a one-chunk sequence of this wave alone: normalise and store, no merge
         if (active) {
           l_run += __shfl_xor(l_run, 16);
           l_run += __shfl_xor(l_run, 32);
           const bool wbad = __any(bad);
-          if (col < nh) {
-            T* o = (T*)P.out + (row0 + col) * D + 4 * quad;
+          if (ecol < nh) {
+            T* o = (T*)P.out + (row0 + ecol) * D + 4 * equad;
             const float nan = __builtin_nanf("");
 #pragma unroll
             for (int nn = 0; nn < NT; ++nn)
@@ -751,20 +761,20 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
       // merge the four waves (fixed order) through LDS
       l_run += __shfl_xor(l_run, 16);
       l_run += __shfl_xor(l_run, 32);
-      if (quad == 0) {
-        sm_m[wave][col] = m_run;
-        sm_l[wave][col] = l_run;
+      if (equad == 0) {
+        sm_m[wave][ecol] = m_run;
+        sm_l[wave][ecol] = l_run;
       }
 #pragma unroll
       for (int nn = 0; nn < NT; ++nn)
-        *reinterpret_cast<f32x4*>(&sm_o[wave][col][16 * nn + 4 * quad]) = acc[nn];
-      if (lane == 0) sm_bad[wave] = bad;
+        *reinterpret_cast<f32x4*>(&sm_o[wave][ecol][16 * nn + 4 * equad]) = acc[nn];
+      if (elane == 0) sm_bad[wave] = bad;
       __syncthreads();
 
       int anybad = 0;
 #pragma unroll
       for (int w = 0; w < NW; ++w) anybad |= sm_bad[w];
-      for (int it = tid; it < nh * (D / 4); it += NT_THREADS) {
+      for (int it = etid; it < nh * (D / 4); it += NT_THREADS) {
         const int hh = it / (D / 4);
         const int d4 = (it - hh * (D / 4)) * 4;
         float M = -INFINITY;
@@ -801,7 +811,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
         stores_done();
         __syncthreads();
         const int grp = p / kMergeFan;
-        if (tid == 0)
+        if (etid == 0)
           pend_before = atomicAdd(P.node_count + ((int64_t)s * HT2 + gt) * P.nodes + grp, 1);
         pend = true;
         pend_s = s;
