@@ -46,10 +46,29 @@ def test_m0_misuse_is_rejected(body, what):
     assert p and any(what in x for x in p), p
 
 
+NOTES = """  - .agpr_count:     0
+    .name:           {name}
+    .private_segment_fixed_size: {size}
+    .vgpr_count:     250
+"""
+
+
+def test_scratch_is_read_from_the_notes_and_rejected():
+    dec = "_ZN2pa12_GLOBAL__N_113decode_kernelIfLi128ELi16ELb1ELb1EEEvNS_12DecodeParamsE"
+    allowed = sorted(codecheck.SCRATCH_ALLOWED)[0]
+    notes = ["AMDGPU Metadata\n amdhsa.kernels:\n" + NOTES.format(name=dec, size=1040)
+             + NOTES.format(name=allowed, size=48)
+             + NOTES.format(name="_ZN2pa12_GLOBAL__N_1other", size=0)]
+    sizes = codecheck.scratch_sizes(notes)
+    assert sizes == {dec: 1040, allowed: 48, "_ZN2pa12_GLOBAL__N_1other": 0}
+    bad = codecheck.scratch_problems(sizes)
+    assert len(bad) == 1 and "1040 bytes" in bad[0] and dec in bad[0]
+
+
 def test_built_library_passes():
     if not os.path.exists(LIB_PATH):
         pytest.skip("libpa.so is not built")
     if not os.path.exists(os.path.join(codecheck.LLVM, "llvm-objdump")):
         pytest.skip("ROCm llvm tools not installed")
     rep = codecheck.check(LIB_PATH)
-    assert rep["code_objects"] >= 1 and rep["lds_dma_loads"] > 0
+    assert rep["code_objects"] >= 1 and rep["lds_dma_loads"] > 0 and rep["kernels"] > 100
