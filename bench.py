@@ -49,7 +49,8 @@ HEADLINE = "gqa_bf16"
 WORKLOAD_TEXT = {
     "gqa_bf16": "bf16 GQA decode step: 128 seqs, 64 q heads / 8 KV heads, head_dim 128, "
                 "block_size 16, log-uniform lengths in [1, 4096], shuffled pool (+10% free); "
-                "pa_cache_write of the 128 new tokens, then pa_decode",
+                "the 128 new tokens stored and every sequence decoded (one "
+                "pa_cache_write_decode launch; two_call_step: the same step as two calls)",
     "long_bf16_bs16": "bf16 long-context split-K decode: 8 seqs, lengths uniform in "
                       "[32768, 131072], 32 q / 8 KV heads, head_dim 128, block_size 16, "
                       "512-token partitions",
