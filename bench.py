@@ -21,6 +21,8 @@ Reported (one JSON line on stdout):
   two_call_step the same step as pa_cache_write + pa_decode, with pa_decode's own roofline
   cache_write   the headline step's pa_cache_write alone (128 tokens), event-timed
   tiny_fp32     the tiny fp32 batch: cache write, decode, and the two as a pair
+  copy_blocks   pa_copy_blocks bursts of 128 and 2048 block pairs (copy-on-write), against
+             8 TB/s, each copy checked bit for bit
   parity     GPU output of the last timed step against the oracle
   also       the same decode-only measurement for the long-context batches, and the
              chunked-prefill and draft-verification batches through pa_multi_token
@@ -310,6 +312,62 @@ def tiny_pair(seed, n):
                 write_then_decode=summary_us(time_calls([pair], n)))
 
 
+def copy_blocks_bytes(pairs, num_kv_heads, block_size, head_dim, elem):
+    """Algorithmic bytes of a pa_copy_blocks call: each pair reads and writes one block
+    (num_kv_heads * block_size * head_dim elements) of each of the two caches."""
+    return pairs * 2 * (num_kv_heads * block_size * head_dim * elem) * 2
+
+
+def copy_blocks_leg(seed, reps=60):
+    """pa_copy_blocks (the device half of copy-on-write) on the GQA pool shape: 8 KV heads,
+    block size 16, head size 128, bf16, 32 KiB a block and cache, 16384 blocks a cache.
+    Two bursts: 128 pairs (one launch: the copies a 128-sequence fork of partly filled
+    last blocks makes) and 2048 pairs (16 launches of 128), each from distinct random
+    source blocks to distinct random destinations, several disjoint sets rotated so that
+    no call finds its blocks in the caches.  After timing, every copied block is checked
+    bit for bit against its source."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_344_amd import binding
+    Hkv, bs, D, N = 8, 16, 128, 16384
+    torch.manual_seed(seed)
+    kc = torch.empty((N, Hkv, bs, D), dtype=torch.bfloat16, device="cuda:0").normal_()
+    vc = torch.empty((N, Hkv, D, bs), dtype=torch.bfloat16, device="cuda:0").normal_()
+    block_bytes = Hkv * bs * D * 2
+    rng = np.random.default_rng(seed)
+    out = {"workload": "pa_copy_blocks on the GQA pool shape (8 KV heads, block_size 16, "
+                       "head_dim 128, bf16; 32 KiB a block and cache, 16384 blocks a cache): "
+                       "random distinct source and destination blocks",
+           "block_bytes_per_cache": block_bytes}
+    for pairs in (128, 2048):
+        perm = rng.permutation(N)
+        nsets = min(8, N // (2 * pairs))
+        sets = [(perm[2 * k * pairs:(2 * k + 1) * pairs], perm[(2 * k + 1) * pairs:(2 * k + 2) * pairs])
+                for k in range(nsets)]
+        calls = [binding.PreparedCopyBlocks(kc, vc, s, d) for s, d in sets]
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        ts = time_calls(calls, reps)
+        nbytes = copy_blocks_bytes(pairs, Hkv, bs, D, 2)
+        r = summary_us(ts)
+        gbps = nbytes / (r["mean_us"] * 1e-6) / 1e9
+        exact = all(torch.equal(kc[torch.as_tensor(d)].view(torch.int16),
+                                kc[torch.as_tensor(s)].view(torch.int16)) and
+                    torch.equal(vc[torch.as_tensor(d)].view(torch.int16),
+                                vc[torch.as_tensor(s)].view(torch.int16)) for s, d in sets)
+        r.update(pairs=pairs, launches=(pairs + 127) // 128, algorithmic_bytes=nbytes,
+                 roofline={"bound": "hbm", "achieved": gbps, "peak": PEAK_GBPS, "unit": "GB/s",
+                           "frac": gbps / PEAK_GBPS},
+                 bit_exact=bool(exact))
+        out[f"pairs_{pairs}"] = r
+        log(f"copy_blocks {pairs} pairs: {r['mean_us']:.1f} us, {gbps:.0f} GB/s = "
+            f"{gbps / PEAK_GBPS:.1%} of 8 TB/s, bit-exact {exact}")
+    del kc, vc
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_ceiling(nbytes=2 << 30, reps=5):
     """A plain 2 GiB device-to-device copy (torch copy_), for context: bytes read plus
     bytes written per second, median of ``reps`` timed copies."""
@@ -588,6 +646,7 @@ def main():
         torch.cuda.empty_cache()
 
     tiny = tiny_pair(args.seed, 100)
+    cow = copy_blocks_leg(args.seed)
     log(f"tiny batch: write + decode {tiny['write_then_decode']['mean_us']:.1f} us")
     copy = copy_ceiling()
     rd = read_ceiling()
@@ -629,6 +688,7 @@ def main():
         "two_call_step": two_call,
         "cache_write": cw,
         "tiny_fp32": tiny,
+        "copy_blocks": cow,
         "also": also,
         "copy_ceiling": copy,
         "read_ceiling": rd,

@@ -109,3 +109,15 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_copy_blocks_bytes_by_enumeration():
+    """Every (pair, cache, element) is read once and written once."""
+    pairs, hkv, bs, d, e = 3, 2, 4, 8, 2
+    count = 0
+    for _p in range(pairs):
+        for _cache in ("k", "v"):
+            for _el in range(hkv * bs * d):
+                count += 2 * e  # one read, one write
+    assert bench.copy_blocks_bytes(pairs, hkv, bs, d, e) == count
+    assert bench.copy_blocks_bytes(128, 8, 16, 128, 2) == 128 * 2 * 32768 * 2
