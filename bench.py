@@ -23,6 +23,7 @@ Reported (one JSON line on stdout):
   tiny_fp32     the tiny fp32 batch: cache write, decode, and the two as a pair
   copy_blocks   pa_copy_blocks bursts of 128 and 2048 block pairs (copy-on-write), against
              8 TB/s, each copy checked bit for bit
+  block_manager host time of the block manager per serving step of the headline batch
   parity     GPU output of the last timed step against the oracle
   also       the same decode-only measurement for the long-context batches, and the
              chunked-prefill and draft-verification batches through pa_multi_token
@@ -368,6 +369,65 @@ def copy_blocks_leg(seed, reps=60):
     return out
 
 
+def block_manager_leg(seed, steps=200):
+    """The host block manager (C++, include/pa_block_manager.h) serving the headline
+    batch's 128 sequences: each brought to its length, then timed steps of one token
+    appended to every sequence (slot ids out) plus an export of the block tables and
+    lengths the kernels read, through the C-ABI with marshalled arrays (what a C caller
+    pays) and through the Python binding; then a 16-way fork (beam search) and one append
+    of parents and children, which makes the copy-on-write copies of shared, partly
+    filled last blocks.  Host time only: nothing here touches the GPU."""
+    import ctypes
+    import time
+    import torch
+    from paged_kv_cache_344_amd import binding, inputs
+    b = inputs.make_batch(HEADLINE, seed)
+    S, bs = b.num_seqs, b.block_size
+    maxb = (int(b.seq_lens.max()) + 2 * steps + 2 * bs) // bs + 1  # room for every append
+    bm = binding.BlockManager(16384, bs, maxb)
+    seqs = [bm.add_sequence() for _ in range(S)]
+    left = [int(x) for x in b.seq_lens]
+    while any(left):
+        act = [s for s, n in zip(seqs, left) if n > 0]
+        bm.append(act)
+        left = [max(0, n - 1) for n in left]
+    L = bm._L
+    ids = (ctypes.c_int32 * S)(*seqs)
+    slots = (ctypes.c_int64 * S)()
+    cs, cd = (ctypes.c_int32 * S)(), (ctypes.c_int32 * S)()
+    nc = ctypes.c_int32()
+    bt = torch.empty((S, maxb), dtype=torch.int32)
+    sl = torch.empty((S,), dtype=torch.int32)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if L.pa_bm_append(bm._h, ids, S, slots, cs, cd, ctypes.byref(nc)) != 0:
+            raise RuntimeError("pa_bm_append failed")
+        if L.pa_bm_export(bm._h, ids, S, bt.data_ptr(), sl.data_ptr()) != 0:
+            raise RuntimeError("pa_bm_export failed")
+    c_us = (time.perf_counter() - t0) / steps * 1e6
+    t0 = time.perf_counter()
+    for _ in range(steps // 4):
+        bm.append(seqs)
+        bm.export(seqs)
+    py_us = (time.perf_counter() - t0) / (steps // 4) * 1e6
+    parents = seqs[:16]
+    t0 = time.perf_counter()
+    children = [bm.fork(p) for p in parents]
+    _, copies = bm.append(parents + children)
+    fork_us = (time.perf_counter() - t0) * 1e6
+    ok = bool((sl.numpy() == b.seq_lens + steps).all())
+    bm.close()
+    log(f"block manager: {c_us:.1f} us a step through the C-ABI, {py_us:.1f} us through the "
+        f"binding (128 appends + table export); 16-way fork + append {fork_us:.0f} us, "
+        f"{len(copies)} copy-on-write copies")
+    return {"workload": "host block manager serving the headline batch's 128 sequences "
+                        "(block_size 16, 16384 blocks): per step one token appended to every "
+                        "sequence plus the export of block tables and lengths",
+            "step_us_c_abi": c_us, "step_us_python_binding": py_us,
+            "fork16_and_append_us": fork_us, "cow_copies": len(copies),
+            "lengths_after_steps_ok": ok}
+
+
 def copy_ceiling(nbytes=2 << 30, reps=5):
     """A plain 2 GiB device-to-device copy (torch copy_), for context: bytes read plus
     bytes written per second, median of ``reps`` timed copies."""
@@ -647,6 +707,7 @@ def main():
 
     tiny = tiny_pair(args.seed, 100)
     cow = copy_blocks_leg(args.seed)
+    bmgr = block_manager_leg(args.seed)
     log(f"tiny batch: write + decode {tiny['write_then_decode']['mean_us']:.1f} us")
     copy = copy_ceiling()
     rd = read_ceiling()
@@ -689,6 +750,7 @@ def main():
         "cache_write": cw,
         "tiny_fp32": tiny,
         "copy_blocks": cow,
+        "block_manager": bmgr,
         "also": also,
         "copy_ceiling": copy,
         "read_ceiling": rd,

@@ -235,8 +235,11 @@ pa_status pa_bm_export(const pa_block_manager* bm, const int32_t* seqs, int32_t 
   for (int32_t i = 0; i < n; ++i) {
     const Sequence& s = *bm->find(seqs[i]);
     int32_t* row = block_tables + (int64_t)i * bm->max_blocks;
-    for (int32_t j = 0; j < bm->max_blocks; ++j)
-      row[j] = j < (int32_t)s.blocks.size() ? s.blocks[(size_t)j] : -1;
+    // the used entries, then -1 to the end of the row (a copy and a fill, not a
+    // per-entry branch: the table is rewritten for every step)
+    const size_t used = s.blocks.size();
+    std::copy(s.blocks.begin(), s.blocks.end(), row);
+    std::fill(row + used, row + bm->max_blocks, -1);
     seq_lens[i] = s.len;
   }
   return PA_OK;

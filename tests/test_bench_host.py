@@ -121,3 +121,12 @@ def test_copy_blocks_bytes_by_enumeration():
                 count += 2 * e  # one read, one write
     assert bench.copy_blocks_bytes(pairs, hkv, bs, d, e) == count
     assert bench.copy_blocks_bytes(128, 8, 16, 128, 2) == 128 * 2 * 32768 * 2
+
+
+def test_block_manager_leg_runs_on_the_host():
+    """The bench's host block-manager leg: every sequence ends at its length plus the
+    timed steps, and the 16-way fork of partly filled last blocks makes 16 copies."""
+    r = bench.block_manager_leg(0, steps=8)
+    assert r["lengths_after_steps_ok"]
+    assert r["cow_copies"] == 16
+    assert r["step_us_c_abi"] > 0 and r["step_us_python_binding"] > 0
