@@ -130,3 +130,22 @@ def test_block_manager_leg_runs_on_the_host():
     assert r["lengths_after_steps_ok"]
     assert r["cow_copies"] == 16
     assert r["step_us_c_abi"] > 0 and r["step_us_python_binding"] > 0
+
+
+def test_waste_leg_matches_the_closed_forms():
+    """Paged slots = sum over requests of ceil(L / bs) * bs; contiguous = S * reservation."""
+    r = bench.waste_leg(0)
+    b = inputs.make_batch(bench.HEADLINE, 0)
+    bs = b.block_size
+    assert r["tokens"] == int(b.seq_lens.sum())
+    assert r["paged_slots"] == sum(-(-int(n) // bs) * bs for n in b.seq_lens)
+    assert r["contiguous_slots"] == b.num_seqs * b.max_blocks_per_seq * bs
+    assert r["admitted_contiguous"] == r["pool_slots"] // (b.max_blocks_per_seq * bs)
+    # paged admission: the longest prefix of requests whose blocks fit the pool
+    used, fit = 0, 0
+    for n in b.seq_lens:
+        used += -(-int(n) // bs) * bs
+        if used > r["pool_slots"]:
+            break
+        fit += 1
+    assert r["admitted_paged"] == fit
