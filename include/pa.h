@@ -78,8 +78,10 @@ typedef struct pa_decode_ext {
   int32_t partition_size;     /* tokens per split-K partition: 0 = default (chosen on  */
                               /* the device from the lengths: one workgroup's even   */
                               /* share of the work, rounded up to a multiple of 256,  */
-                              /* at least 512), < 0 = never split, > 0 = that many    */
-                              /* (a multiple of 32)                                    */
+                              /* or 3/4 of it when no sequence would be split but the */
+                              /* (sequence, head) units outnumber the workgroups; at  */
+                              /* least 512), < 0 = never split, > 0 = that many (a    */
+                              /* multiple of 32)                                      */
   int32_t dtype;              /* pa_dtype of q, k_cache, v_cache and out               */
   void* workspace;            /* device scratch: queue, counters, split-K partials;    */
                               /* caller-owned, zero-filled before first use            */

@@ -177,6 +177,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   __shared__ int sm_cbase[kSizeClasses];
   __shared__ int sm_wsum[NW];
   __shared__ float sm_wsumf[NW];
+  __shared__ int sm_wmax[NW], sm_wcnt[NW];
   __shared__ int sm_next[2];  // by item parity: an item may pass no barrier before the next write
   __shared__ int sm_flag[2];
 #ifdef PA_DECODE_TRACE
@@ -201,7 +202,9 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   // and, when split, partial results to write and merge later, which costs about as
   // much per item whatever its length, so partitions are made as long as the load
   // balance allows: kPartShare times one workgroup's even share of all the (token, KV
-  // head tile) work, rounded up to a multiple of 256 tokens, never below part_tokens.
+  // head tile) work, rounded up to a multiple of 256 tokens, never below part_tokens
+  // (kTailShare of the share instead when at that length no sequence would be split
+  // but there are more units than workgroups).
   // Every workgroup computes the same sum in the same order, so all choose alike.
   // Then: the number of full partitions of each sequence and the class of its last one
   // (0: an empty or invalid sequence, a one-item fill; 1: one chunk; 2 ..
@@ -209,6 +212,7 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
   {
     int Ls[4];
     float lsum = 0.f;
+    int lmax = 0, lcnt = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = 4 * tid + i;
@@ -220,18 +224,37 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
         if (L > 0 && L <= P.max_tokens) Ls[i] = L;
       }
       lsum += (float)Ls[i];
+      lmax = max(lmax, Ls[i]);
+      lcnt += Ls[i] > 0;
     }
     if (P.auto_part) {
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
-      if (lane == 0) sm_wsumf[wave] = lsum;
+      for (int o = 32; o >= 1; o >>= 1) {
+        lsum += __shfl_xor(lsum, o);
+        lmax = max(lmax, __shfl_xor(lmax, o));
+        lcnt += __shfl_xor(lcnt, o);
+      }
+      if (lane == 0) {
+        sm_wsumf[wave] = lsum;
+        sm_wmax[wave] = lmax;
+        sm_wcnt[wave] = lcnt;
+      }
       __syncthreads();
       float tot = 0.f;
+      int mx = 0, cnt = 0;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) tot += sm_wsumf[w];
+      for (int w = 0; w < NW; ++w) {
+        tot += sm_wsumf[w];
+        mx = max(mx, sm_wmax[w]);
+        cnt += sm_wcnt[w];
+      }
       const float share = tot * (float)HT2 / (float)gridDim.x;  // tokens per workgroup
-      const float want = fminf(kPartShare * share, (float)P.max_tokens);
-      PT = max(PT, (int)ceilf(want * (1.f / 256.f)) * 256);
+      int pt = (int)ceilf(fminf(kPartShare * share, (float)P.max_tokens) * (1.f / 256.f)) * 256;
+      // no sequence would be split, yet there are more (sequence, head tile) units than
+      // workgroups: the longest units would set the tail, so split them after all
+      if (pt >= mx && (int64_t)cnt * HT2 > (int64_t)gridDim.x)
+        pt = (int)ceilf(fminf(kTailShare * share, (float)P.max_tokens) * (1.f / 256.f)) * 256;
+      PT = max(PT, pt);
     }
 #ifdef PA_DECODE_TRACE
     if (threadIdx.x == 0) tr[248] = PA_TRACE_STAMP();

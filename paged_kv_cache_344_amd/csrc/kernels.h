@@ -12,6 +12,7 @@ constexpr int kMergeFan = 16;       // partials combined per merge node
 constexpr int kMaxPartitions = 8192;
 constexpr int kSizeClasses = 17;    // classes the last partitions are ordered by
 constexpr float kPartShare = 1.0f;  // default partition: this fraction of a workgroup's share
+constexpr float kTailShare = 0.75f;  // ... when at that length no sequence would be split
 constexpr size_t kStaticScratchBytes = size_t(64) << 20;  // pa_decode_noalloc's device scratch
 constexpr int kPartSlot = 16;       // int32 slot of the decode workspace header (byte 64) that
                                     // records the partition length the last launch used
