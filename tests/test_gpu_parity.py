@@ -449,3 +449,45 @@ def test_default_partitioning_lengthens_partitions():
     say(f"default partitioning, many items: {check_close(auto, ref, 'bf16', 'default, many items')}")
     np.testing.assert_array_equal(g.out_f64(g.decode(0)), auto)
     say(f"explicit 512: {check_close(g.out_f64(g.decode(512)), ref, 'bf16', 'explicit 512')}")
+
+
+def _documented_partition(b, grid):
+    """The default partition length as include/pa.h states it: one workgroup's even share
+    of the (token, KV head tile) work, rounded up to a multiple of 256 tokens, or 3/4 of
+    the share when at that length no sequence would be split but the (sequence, head
+    tile) units outnumber the workgroups; at least 512."""
+    max_tokens = b.max_blocks_per_seq * b.block_size
+    lens = [int(n) for n in b.seq_lens if 0 < int(n) <= max_tokens]
+    g = b.num_q_heads // b.num_kv_heads
+    ht2 = b.num_kv_heads * -(-g // 16)
+    share = sum(lens) * ht2 / grid
+
+    def up256(x):
+        return -(-int(np.ceil(min(x, max_tokens))) // 256) * 256
+    pt = up256(1.0 * share)
+    if pt >= max(lens) and len(lens) * ht2 > grid:
+        pt = up256(0.75 * share)
+    return max(512, pt)
+
+
+@pytest.mark.parametrize("name,want", [("gqa_bf16", 1536), ("mha_fp16", 1792),
+                                       ("prefix_bf16", 1536), ("long_bf16_bs16_default", 8448)])
+def test_default_partition_rule_on_the_benchmark_batches(name, want):
+    """The partition length the device chooses equals the documented rule (two workgroups
+    a compute unit: these batches have more units than that), and, on MI355X's 256
+    compute units, the length the measurements in the design notes were taken at."""
+    import paged_kv_cache_344_amd as pa
+    b = inputs.make_batch(name, seed=0)
+    g = OnGpu(b)
+    ws = pa.workspace_for(g.q, g.block_tables, b.num_blocks, b.block_size, b.num_kv_heads,
+                          partition_size=0)
+    out = torch.empty_like(g.q)
+    say(f"pa_decode {name} default partitioning (rule check)")
+    pa.pa_decode(g.q, g.k_cache, g.v_cache, g.block_tables, g.seq_lens, b.block_size,
+                 b.num_kv_heads, b.scale, out, workspace=ws, partition_size=0,
+                 shared_blocks=b.shared_blocks > 0)
+    used = pa.decode_partition_used(ws)
+    grid = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    assert used == _documented_partition(b, grid), (name, used, grid)
+    if grid == 512:
+        assert used == want, (name, used)
