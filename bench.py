@@ -199,10 +199,14 @@ class Copy:
 
 
 def time_steps(copies, steps, warmup, with_write, fused=False):
-    """Run warmup + timed steps rotating over copies; returns (elapsed_s, [call_ms]).
+    """Run warmup + timed steps rotating over copies; returns (elapsed_s, region_ms,
+    [call_ms]).
     A step is the decode call, preceded by the batch's cache write when with_write; with
-    fused, write and decode are the one pa_cache_write_decode call.  The events bracket
-    the decode call (the fused call when fused)."""
+    fused, write and decode are the one pa_cache_write_decode call.  The timed steps run
+    twice: first with nothing else in the stream (elapsed_s, bracketed by device
+    synchronisation; region_ms: an event pair around them, divided by the steps), then
+    with an event pair around each decode call (the fused call when fused) for the
+    per-call spread, so that per-call event records are not part of the throughput."""
     import torch
     n = len(copies)
 
@@ -222,15 +226,21 @@ def time_steps(copies, steps, warmup, with_write, fused=False):
     for k in range(warmup):
         run(copies[k % n])
     torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    r0.record()
+    for k in range(steps):
+        run(copies[k % n])
+    r1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    region_ms = r0.elapsed_time(r1) / steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for k in range(steps):
         run(copies[k % n], ev[k])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    return elapsed, [a.elapsed_time(z) for a, z in ev]
+    return elapsed, region_ms, [a.elapsed_time(z) for a, z in ev]
 
 
 def oracle_reference(b):
@@ -582,15 +592,24 @@ def measure(name, seed, steps, warmup, copies_min, with_write, fused=False):
     part = b.partition_size
     copies = [Copy(b, part) for _ in range(n_copies)]
     torch.cuda.synchronize()
-    elapsed, dms = time_steps(copies, steps, warmup, with_write, fused)
+    elapsed, region_ms, dms = time_steps(copies, steps, warmup, with_write, fused)
     dec_bytes = decode_bytes(b)
     if fused and b.slot_mapping is not None:  # the timed call also stores the new tokens
         dec_bytes += cache_write_bytes(b)
-    mean_ms = sum(dms) / len(dms)
+    # a step that is the one launch measured: its mean duration is the timed region's
+    # (an event pair around all the steps, divided by their number), which includes any
+    # gap between launches but no per-call event records; otherwise the per-call events'
+    one_launch = fused or not with_write or b.slot_mapping is None
+    mean_ms = region_ms if one_launch else sum(dms) / len(dms)
     srt = sorted(dms)
     if b.query_start is not None:
         dec_bytes = multi_token_bytes(b)
     res = dict(batch=b, copies=copies, elapsed=elapsed, decode_ms=mean_ms,
+               decode_ms_event_pairs=sum(dms) / len(dms),
+               call_timing=("mean: an event pair around the timed steps, divided by their "
+                            "number; p10 / p90: an event pair around each call in a second "
+                            "run of the steps (each pair adds its own ~1-2 us)"
+                            if one_launch else "an event pair around each call"),
                decode_ms_p10=srt[len(srt) // 10], decode_ms_p90=srt[(9 * len(srt)) // 10],
                decode_bytes=dec_bytes, write_bytes=cache_write_bytes(b) if with_write else 0,
                gbps=dec_bytes / (mean_ms * 1e-3) / 1e9, n_copies=n_copies)
@@ -650,7 +669,8 @@ def main():
     head_out = last.out.clone()  # the last timed step's output, for the parity check
 
     # the same step as two calls, pa_cache_write then pa_decode (same copies), for context
-    el2, dms2 = time_steps(head["copies"], args.steps, args.warmup, with_write=True, fused=False)
+    el2, _, dms2 = time_steps(head["copies"], args.steps, args.warmup, with_write=True,
+                              fused=False)
     dec_bytes = decode_bytes(b)
     dec_ms = sum(dms2) / len(dms2)
     two_call = {"value": args.steps * tokens / el2, "unit": "tokens/s",
@@ -703,6 +723,7 @@ def main():
             also[name] = dict(workload=WORKLOAD_TEXT.get(name, name),
                               new_tokens=int(rb.query_start[-1]), sum_L=rb.total_tokens(),
                               call_us=r["decode_ms"] * 1e3, call_us_p10=r["decode_ms_p10"] * 1e3,
+                              call_us_event_pairs=r["decode_ms_event_pairs"] * 1e3,
                               call_us_p90=r["decode_ms_p90"] * 1e3, algorithmic_flops=fl,
                               roofline=roof, algorithmic_bytes=r["decode_bytes"],
                               achieved_gbps=r["gbps"],
@@ -719,6 +740,7 @@ def main():
                           partition_used=used,
                           tokens_per_s=rb.total_tokens() / (r["decode_ms"] * 1e-3),
                           decode_us=r["decode_ms"] * 1e3, decode_us_p10=r["decode_ms_p10"] * 1e3,
+                          decode_us_event_pairs=r["decode_ms_event_pairs"] * 1e3,
                           decode_us_p90=r["decode_ms_p90"] * 1e3,
                           algorithmic_bytes=r["decode_bytes"], achieved_gbps=r["gbps"],
                           frac_of_peak=r["gbps"] / PEAK_GBPS)
@@ -766,6 +788,8 @@ def main():
                                "partitions and the split-K merge in the same launch)",
                      "algorithmic_bytes_per_call": head["decode_bytes"],
                      "mean_call_us": head["decode_ms"] * 1e3,
+                     "call_timing": head["call_timing"],
+                     "event_pair_mean_call_us": head["decode_ms_event_pairs"] * 1e3,
                      "p10_call_us": head["decode_ms_p10"] * 1e3,
                      "p90_call_us": head["decode_ms_p90"] * 1e3},
         "cpu_baseline": cpu,
