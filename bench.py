@@ -402,7 +402,7 @@ def block_manager_leg(seed, steps=200):
         act = [s for s, n in zip(seqs, left) if n > 0]
         bm.append(act)
         left = [max(0, n - 1) for n in left]
-    L = bm._L
+    L, h = binding.lib(), bm.handle
     ids = (ctypes.c_int32 * S)(*seqs)
     slots = (ctypes.c_int64 * S)()
     cs, cd = (ctypes.c_int32 * S)(), (ctypes.c_int32 * S)()
@@ -411,9 +411,9 @@ def block_manager_leg(seed, steps=200):
     sl = torch.empty((S,), dtype=torch.int32)
     t0 = time.perf_counter()
     for _ in range(steps):
-        if L.pa_bm_append(bm._h, ids, S, slots, cs, cd, ctypes.byref(nc)) != 0:
+        if L.pa_bm_append(h, ids, S, slots, cs, cd, ctypes.byref(nc)) != 0:
             raise RuntimeError("pa_bm_append failed")
-        if L.pa_bm_export(bm._h, ids, S, bt.data_ptr(), sl.data_ptr()) != 0:
+        if L.pa_bm_export(h, ids, S, bt.data_ptr(), sl.data_ptr()) != 0:
             raise RuntimeError("pa_bm_export failed")
     c_us = (time.perf_counter() - t0) / steps * 1e6
     t0 = time.perf_counter()

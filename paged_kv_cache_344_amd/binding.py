@@ -528,6 +528,12 @@ class BlockManager:
                               ctypes.byref(h)), "pa_bm_create")
         self._h = h
 
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        """The pa_block_manager* of include/pa_block_manager.h, for callers that drive the
+        C functions (``lib().pa_bm_*``) with arrays of their own."""
+        return self._h
+
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:
             self._L.pa_bm_destroy(self._h)
