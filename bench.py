@@ -30,6 +30,8 @@ Reported (one JSON line on stdout):
              chunked-prefill and draft-verification batches through pa_multi_token
              (against the roof each meets first: MFMA flops or HBM bytes); each warms
              up W steps and then until the device has been busy SECONDARY_WARM_MS
+  read_probe what a read-only kernel (pa_read_probe) gets from HBM over 2 GiB in 4 KiB
+             tiles, front to back and in a random order; copy_reference a torch copy
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -134,26 +136,46 @@ def multi_token_bytes(b):
             b.head_dim * e + 4 * nb + 8 * b.num_seqs + 4)
 
 
-def read_ceiling(nbytes=2 << 30, reps=5):
-    """A plain read of 2 GiB (torch sum of a bf16 tensor), for context: bytes read per
-    second, median of ``reps`` timed reductions."""
+def read_probe(nbytes=2 << 30, reps=20):
+    """What a kernel that does nothing but read gets from HBM (pa_read_probe): 2 GiB in
+    4 KiB tiles, front to back and in a random order (the granule and the placement of a
+    shuffled block pool), one 16-byte non-temporal load per thread and tile.  After 50 ms
+    of untimed launches, the median of ``reps`` launches timed with an event pair each;
+    bytes are the tiles' (the random order also reads 2 MiB of tile ids)."""
     import torch
-    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda:0")
-    x.sum()
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        x.sum(dtype=torch.float32)
-        e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e-3)
-    t = sorted(ts)[len(ts) // 2]
-    del x
+    from paged_kv_cache_344_amd import binding
+    lib = binding.lib()
+    sink_bytes = 2048 * 4 * 4  # PA_READ_PROBE_SINK_BYTES
+    x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    n = nbytes // 4096
+    perm = torch.randperm(n, dtype=torch.int32, device="cuda:0")
+    sink = torch.empty(sink_bytes // 4, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch(tiles):
+        st = lib.pa_read_probe(x.data_ptr(), nbytes, tiles, n, sink.data_ptr(), sink_bytes, stream)
+        if st != 0:
+            raise RuntimeError(f"pa_read_probe: {lib.pa_last_error().decode()}")
+    out = {"bytes_read": nbytes,
+           "what": "pa_read_probe: 2 GiB read once in 4 KiB tiles, 16-byte non-temporal loads"}
+    for name, tiles in (("stream", None), ("random_4k_tiles", perm.data_ptr())):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.05:
+            launch(tiles)
+            torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch(tiles)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = sorted(ts)[len(ts) // 2]
+        out[name] = {"gbps": nbytes / t / 1e9, "frac": nbytes / t / 1e9 / PEAK_GBPS, "seconds": t}
+    del x, perm, sink
     torch.cuda.empty_cache()
-    return {"gbps": nbytes / t / 1e9, "bytes_read": nbytes, "seconds": t,
-            "what": "torch sum over a 2 GiB bf16 tensor, bytes read"}
+    return out
 
 
 def cache_write_bytes(b):
@@ -474,7 +496,7 @@ def waste_leg(seed, pool_slots=65536):
             "pool_slots": pool_slots, "admitted_contiguous": cont, "admitted_paged": paged}
 
 
-def copy_ceiling(nbytes=2 << 30, reps=5):
+def copy_reference(nbytes=2 << 30, reps=5):
     """A plain 2 GiB device-to-device copy (torch copy_), for context: bytes read plus
     bytes written per second, median of ``reps`` timed copies."""
     import torch
@@ -769,10 +791,12 @@ def main():
     bmgr = block_manager_leg(args.seed)
     wst = waste_leg(args.seed)
     log(f"tiny batch: write + decode {tiny['write_then_decode']['mean_us']:.1f} us")
-    copy = copy_ceiling()
-    rd = read_ceiling()
-    log(f"device read ceiling: {rd['gbps']:.0f} GB/s = {rd['gbps'] / PEAK_GBPS:.1%} of 8 TB/s")
-    log(f"device copy ceiling: {copy['gbps']:.0f} GB/s = {copy['gbps'] / PEAK_GBPS:.1%} of 8 TB/s")
+    copy = copy_reference()
+    rd = read_probe()
+    log(f"read probe, 2 GiB: front to back {rd['stream']['gbps']:.0f} GB/s = "
+        f"{rd['stream']['frac']:.1%} of 8 TB/s; random 4 KiB tiles "
+        f"{rd['random_4k_tiles']['gbps']:.0f} GB/s = {rd['random_4k_tiles']['frac']:.1%}")
+    log(f"torch copy of 2 GiB: {copy['gbps']:.0f} GB/s = {copy['gbps'] / PEAK_GBPS:.1%} of 8 TB/s")
     traffic = measured_traffic(f"{HEADLINE}/pa_cache_write_decode", head["decode_bytes"])
     line = {
         "metric": METRIC,
@@ -815,8 +839,8 @@ def main():
         "block_manager": bmgr,
         "waste": wst,
         "also": also,
-        "copy_ceiling": copy,
-        "read_ceiling": rd,
+        "copy_reference": copy,
+        "read_probe": rd,
     }
     print(json.dumps(line), flush=True)
     return 0

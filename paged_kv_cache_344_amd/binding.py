@@ -91,6 +91,8 @@ def lib():
         L.pa_multi_token_workspace_bytes.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(CopyBlocksExt)]
         L.pa_copy_blocks.restype = ctypes.c_int
+        L.pa_read_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int64, vp, ctypes.c_size_t, vp]
+        L.pa_read_probe.restype = ctypes.c_int
         P32, P64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
         L.pa_bm_create.argtypes = [ctypes.c_int64, i32, i32, vp, ctypes.POINTER(vp)]
         L.pa_bm_destroy.argtypes = [vp]
@@ -120,7 +122,7 @@ def lib():
     return _lib
 
 
-HEADERS = ("pa.h", "pa_block_manager.h")
+HEADERS = ("pa.h", "pa_block_manager.h", "pa_probe.h")
 
 
 def header_functions() -> list:

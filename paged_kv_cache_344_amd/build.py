@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libpa.so")
 # diagnostic build: the same library with the decode kernel recording per-item timestamps
 TRACE_LIB_PATH = os.path.join(PKG, "libpa_trace.so")
 SOURCES = ["decode.hip", "cache_write.hip", "copy_blocks.hip", "multi_token.hip", "noalloc.hip",
-           "pa_api.cpp", "block_manager.cpp"]
+           "read_probe.hip", "pa_api.cpp", "block_manager.cpp"]
 
 
 def hipcc() -> str:

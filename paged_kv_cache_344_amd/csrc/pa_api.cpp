@@ -17,7 +17,12 @@
 
 #include "kernels.h"
 #include "pa.h"
+#include "pa_probe.h"
+#include "read_probe.h"
 
+static_assert(PA_READ_PROBE_TILE == pa::kProbeTile &&
+                  PA_READ_PROBE_SINK_BYTES == (size_t)pa::kProbeGrid * pa::kProbeWaves * 4,
+              "pa_probe.h and the read probe disagree on its tile or sink size");
 static_assert(PA_NOALLOC_SCRATCH_BYTES == pa::kStaticScratchBytes,
               "pa.h and the library disagree on the no-allocation scratch size");
 
@@ -569,6 +574,28 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const
     const hipError_t e = pa::launch_copy_blocks(p, stream);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "copy launch: %s", hipGetErrorString(e));
   }
+  return PA_OK;
+}
+
+pa_status pa_read_probe(const void* src, size_t src_bytes, const int32_t* tiles,
+                        int64_t n_tiles, void* sink, size_t sink_bytes, void* stream) {
+  g_error.clear();
+  if (n_tiles < 0) return fail(PA_ERR_INVALID_ARG, "n_tiles %lld < 0", (long long)n_tiles);
+  if (src_bytes % PA_READ_PROBE_TILE)
+    return fail(PA_ERR_INVALID_ARG, "src_bytes %zu is not a multiple of %d", src_bytes, PA_READ_PROBE_TILE);
+  const int64_t in_src = (int64_t)(src_bytes / PA_READ_PROBE_TILE);
+  if (!tiles && n_tiles > in_src)
+    return fail(PA_ERR_INVALID_ARG, "n_tiles %lld > %lld tiles in src", (long long)n_tiles, (long long)in_src);
+  if (sink_bytes < PA_READ_PROBE_SINK_BYTES)
+    return fail(PA_ERR_INVALID_ARG, "sink_bytes %zu < %zu", sink_bytes, (size_t)PA_READ_PROBE_SINK_BYTES);
+  if (n_tiles == 0) return PA_OK;
+  if (!src || !sink) return fail(PA_ERR_INVALID_ARG, "src or sink is NULL");
+  if (!aligned(src, 16) || !aligned(sink, 4) || (tiles && !aligned(tiles, 4)))
+    return fail(PA_ERR_INVALID_ARG, "src must be 16-byte aligned, sink and tiles 4-byte aligned");
+  const hipError_t e = pa::launch_read_probe(static_cast<const char*>(src), in_src, tiles, n_tiles,
+                                             static_cast<uint32_t*>(sink),
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "read probe launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
 

@@ -404,3 +404,35 @@ def test_multi_token_split_rejects(lib, kw, want):
     assert lib.pa_last_error()
     if kw.get("partition_size") == 100:
         assert _mt_ws(lib, partition_size=100)[0] == B.PA_ERR_INVALID_ARG
+
+
+# ---- pa_read_probe (include/pa_probe.h): every rejection happens before any HIP call
+
+SINK = 2048 * 4 * 4  # PA_READ_PROBE_SINK_BYTES
+
+
+def test_read_probe_header_constants():
+    head = open(os.path.join(B.INCLUDE, "pa_probe.h")).read()
+    assert "#define PA_READ_PROBE_TILE 4096" in head
+    assert "#define PA_READ_PROBE_SINK_BYTES ((size_t)2048 * 4 * 4)" in head
+
+
+@pytest.mark.parametrize("args", [
+    (FAKE, 8192, None, -1, FAKE, SINK),        # negative tile count
+    (FAKE, 8000, None, 1, FAKE, SINK),         # size not a multiple of 4096
+    (FAKE, 8192, None, 3, FAKE, SINK),         # more tiles than the buffer holds, no list
+    (FAKE, 8192, None, 1, FAKE, SINK - 4),     # sink too small
+    (None, 8192, None, 1, FAKE, SINK),         # NULL source
+    (FAKE, 8192, None, 1, None, SINK),         # NULL sink
+    (FAKE + 8, 8192, None, 1, FAKE, SINK),     # source not 16-byte aligned
+    (FAKE, 8192, None, 1, FAKE + 2, SINK),     # sink not 4-byte aligned
+    (FAKE, 8192, FAKE + 2, 5, FAKE, SINK),     # tile list not 4-byte aligned
+])
+def test_read_probe_rejects(lib, args):
+    assert lib.pa_read_probe(*args, None) == B.PA_ERR_INVALID_ARG
+    assert lib.pa_last_error()
+
+
+def test_read_probe_nothing_to_do(lib):
+    """No tiles: PA_OK without a launch, whatever the pointers."""
+    assert lib.pa_read_probe(None, 0, None, 0, None, SINK, None) == B.PA_OK
