@@ -797,6 +797,10 @@ def main():
         f"{rd['stream']['frac']:.1%} of 8 TB/s; random 4 KiB tiles "
         f"{rd['random_4k_tiles']['gbps']:.0f} GB/s = {rd['random_4k_tiles']['frac']:.1%}")
     log(f"torch copy of 2 GiB: {copy['gbps']:.0f} GB/s = {copy['gbps'] / PEAK_GBPS:.1%} of 8 TB/s")
+    # the headline step's rate against what a read-only kernel gets from shuffled tiles
+    rd["headline_over_random_4k_tiles"] = head["gbps"] / rd["random_4k_tiles"]["gbps"]
+    log(f"headline step: {rd['headline_over_random_4k_tiles']:.1%} of the read probe's "
+        f"random-tile rate")
     traffic = measured_traffic(f"{HEADLINE}/pa_cache_write_decode", head["decode_bytes"])
     line = {
         "metric": METRIC,
