@@ -143,22 +143,17 @@ def read_probe(nbytes=2 << 30, reps=20):
     of untimed launches, the median of ``reps`` launches timed with an event pair each;
     bytes are the tiles' (the random order also reads 2 MiB of tile ids)."""
     import torch
-    from paged_kv_cache_344_amd import binding
-    lib = binding.lib()
-    sink_bytes = 2048 * 4 * 4  # PA_READ_PROBE_SINK_BYTES
+    import paged_kv_cache_344_amd as pa
     x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
     n = nbytes // 4096
     perm = torch.randperm(n, dtype=torch.int32, device="cuda:0")
-    sink = torch.empty(sink_bytes // 4, dtype=torch.int32, device="cuda:0")
-    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.empty(pa.binding.READ_PROBE_SINK_BYTES // 4, dtype=torch.int32, device="cuda:0")
 
     def launch(tiles):
-        st = lib.pa_read_probe(x.data_ptr(), nbytes, tiles, n, sink.data_ptr(), sink_bytes, stream)
-        if st != 0:
-            raise RuntimeError(f"pa_read_probe: {lib.pa_last_error().decode()}")
+        pa.pa_read_probe(x, n, sink, tiles=tiles)
     out = {"bytes_read": nbytes,
            "what": "pa_read_probe: 2 GiB read once in 4 KiB tiles, 16-byte non-temporal loads"}
-    for name, tiles in (("stream", None), ("random_4k_tiles", perm.data_ptr())):
+    for name, tiles in (("stream", None), ("random_4k_tiles", perm)):
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < 0.05:
             launch(tiles)

@@ -7,5 +7,5 @@ from .binding import (BlockManager, PaError, PreparedCacheWrite,  # noqa: F401
                       PreparedCopyBlocks, PreparedDecode, PreparedMultiToken, pa_cache_write,
                       pa_cache_write_decode,
                       pa_copy_blocks, pa_decode, pa_decode_noalloc, pa_decode_workspace_bytes,
-                      pa_multi_token,
+                      pa_multi_token, pa_read_probe,
                       decode_partition_used, workspace_for)

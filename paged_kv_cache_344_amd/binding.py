@@ -510,6 +510,27 @@ def pa_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src, dst, *,
     PreparedCopyBlocks(k_cache, v_cache, src, dst, stream=stream)()
 
 
+READ_PROBE_SINK_BYTES = 2048 * 4 * 4  # PA_READ_PROBE_SINK_BYTES of include/pa_probe.h
+
+
+def pa_read_probe(src: torch.Tensor, n_tiles: int, sink: torch.Tensor,
+                  tiles: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Read n_tiles 4 KiB tiles of src once each (include/pa_probe.h): tiles 0 ..
+    n_tiles-1 in order, or the int32 ids in ``tiles``; sink (at least
+    READ_PROBE_SINK_BYTES bytes) receives an XOR fold of what was read.  A measurement
+    aid: what a read-only kernel gets from HBM."""
+    dev = src.device
+    _need(src.is_cuda and src.is_contiguous(), "src must be a contiguous device tensor")
+    _need(sink.device == dev and sink.is_contiguous(), "sink placement")
+    if tiles is not None:
+        _need(tiles.device == dev and tiles.dtype == torch.int32 and tiles.is_contiguous()
+              and tiles.numel() >= n_tiles, "tiles must be int32 on src's device, n_tiles long")
+    _check(lib().pa_read_probe(src.data_ptr(), src.numel() * src.element_size(),
+                               None if tiles is None else tiles.data_ptr(), int(n_tiles),
+                               sink.data_ptr(), sink.numel() * sink.element_size(),
+                               _stream_ptr(dev, stream)), "pa_read_probe")
+
+
 class BlockManager:
     """The host block manager of include/pa_block_manager.h: one C object per
     instance, freed with the instance (or by ``close()``)."""

@@ -415,6 +415,7 @@ def test_read_probe_header_constants():
     head = open(os.path.join(B.INCLUDE, "pa_probe.h")).read()
     assert "#define PA_READ_PROBE_TILE 4096" in head
     assert "#define PA_READ_PROBE_SINK_BYTES ((size_t)2048 * 4 * 4)" in head
+    assert B.READ_PROBE_SINK_BYTES == SINK
 
 
 @pytest.mark.parametrize("args", [
