@@ -213,14 +213,25 @@ __global__ __launch_bounds__(NT_THREADS, sizeof(T) == 2 ? 2 : 1) void decode_ker
     int Ls[4];
     float lsum = 0.f;
     int lmax = 0, lcnt = 0;
+    // every load first, from an index clamped into the launch's S >= 1 sequences, so
+    // that all of them are in flight together: behind the per-sequence test below the
+    // compiler issued them one at a time, each waiting for the one before
+    int Lr[4];
+    int64_t slot_r[4] = {};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sc = min(4 * tid + i, S - 1);
+      Lr[i] = P.seq_lens[sc];
+      if constexpr (FUSE) slot_r[i] = P.slot_mapping[sc];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = 4 * tid + i;
       Ls[i] = 0;
       if (s < S) {
-        const int L = P.seq_lens[s];
+        const int L = Lr[i];
         sm_len[s] = L;
-        if constexpr (FUSE) sm_slot[s] = P.slot_mapping[s];
+        if constexpr (FUSE) sm_slot[s] = slot_r[i];
         if (L > 0 && L <= P.max_tokens) Ls[i] = L;
       }
       lsum += (float)Ls[i];
