@@ -49,15 +49,18 @@ def _decode(g, part):
 
 
 @pytest.mark.parametrize("name", ["long_bf16_bs16", "long_bf16_bs32", "long_bf16_bs16_default",
-                                  "long_bf16_bs32_default"])
+                                  "long_bf16_bs32_default", "long_bf16_bs16_nosplit"])
 def test_full_size_long_context_every_output(name):
     """The long-context batch (seed 0, the measured one) in the launch configuration the
-    benchmark times: every sequence, every head."""
+    benchmark times: every sequence, every head (also unsplit: one item per sequence and
+    KV head, every partition as long as the table's capacity)."""
     b = inputs.make_batch(name, seed=0)
     g = OnGpu(b)
     got, used = _decode(g, b.partition_size)
-    if b.partition_size:
+    if b.partition_size > 0:
         assert used == b.partition_size
+    elif b.partition_size < 0:
+        assert used >= int(b.seq_lens.max()), used
     ref = oracle_decode(b)
     rep = check_close(got, ref, b.dtype, f"{name} full")
     say(f"parity {name} (partition {used}): {rep}")
