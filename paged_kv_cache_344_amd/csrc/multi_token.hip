@@ -311,7 +311,12 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? (ONE_TILE ? 2 : 3) : 1) v
   const bool split = P.parts > 1;
 
   const int G = P.group, Hq = P.num_q_heads;
+  // the sequence's query range and length, read together (one round trip, not two):
+  // the empty asm keeps the length's load ahead of the early returns, below which the
+  // compiler would otherwise sink it
   const int q0 = P.query_start[s], q1 = P.query_start[s + 1];
+  const int L = P.seq_lens[s];
+  asm volatile("" ::"s"(L));
   const int n = q1 - q0;
   // rows that cannot be placed inside out[0 .. T) are never written
   if (q0 < 0 || n < 0 || q1 > P.num_tokens) return;
@@ -319,7 +324,6 @@ __global__ __launch_bounds__(THREADS, sizeof(T) == 2 ? (ONE_TILE ? 2 : 3) : 1) v
   const int R0 = x * ROWS;
   if (R0 >= nrows) return;
   const int rend = min(nrows, R0 + ROWS);
-  const int L = P.seq_lens[s];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -734,6 +738,8 @@ __global__ __launch_bounds__(THREADS) void multi_token_merge_kernel(MultiTokenPa
   const int s = group / P.num_kv_heads;
   const int G = P.group, Hq = P.num_q_heads;
   const int q0 = P.query_start[s], q1 = P.query_start[s + 1];
+  const int L = P.seq_lens[s];  // read beside the query range: one round trip
+  asm volatile("" ::"s"(L));    // (kept ahead of the early return)
   const int n = q1 - q0;
   if (q0 < 0 || n < 0 || q1 > P.num_tokens) return;
   const int R0 = x * ROWS;
@@ -744,7 +750,6 @@ __global__ __launch_bounds__(THREADS) void multi_token_merge_kernel(MultiTokenPa
   const int rr = R0 + r;
   T* o = (T*)P.out + ((int64_t)(q0 + rr / G) * Hq + g * G + rr % G) * D + d4;
   const float nan = __builtin_nanf("");
-  const int L = P.seq_lens[s];
   if (L > P.max_tokens || n > L) {
     store4(o, f32x4{nan, nan, nan, nan});
     return;
