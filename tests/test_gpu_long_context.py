@@ -66,6 +66,18 @@ def test_full_size_long_context_every_output(name):
     say(f"parity {name} (partition {used}): {rep}")
 
 
+@pytest.mark.parametrize("seed", [1, 2])
+def test_full_size_long_context_default_other_seeds(seed):
+    """The default partitioning on the input recipe's other seeds: other lengths, so the
+    device picks other partition lengths (the rule of include/pa.h), every output."""
+    b = inputs.make_batch("long_bf16_bs16_default", seed=seed)
+    g = OnGpu(b)
+    got, used = _decode(g, b.partition_size)
+    assert used % 256 == 0 and used >= 512, used
+    rep = check_close(got, oracle_decode(b), b.dtype, f"long default seed {seed}")
+    say(f"parity long default seed {seed} (partition {used}): {rep}")
+
+
 def _spots(L, P):
     n = (L + P - 1) // P
     last_group = ((n - 1) // FAN) * FAN
